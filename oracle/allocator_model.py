@@ -1,0 +1,191 @@
+"""Reference model of the ref-counted free-list block allocator.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).  The C++ allocator in the
+library is checked against this model op by op on random op sequences.
+
+Semantics follow [P3] section 二 (BlockManager, BlockTable, copy-on-write) and
+[P1] "PagedAttention分页内存管理原理" / "vLLM调度器与PagedAttention协同工作"
+(all blocks are the same size, so a plain free list suffices; blocks are
+allocated on demand when a token crosses a block boundary; shared prefixes are
+tracked with reference counts).  The page's listing lost most of its operators
+in extraction; the readings taken here:
+
+* the free list starts as ``[0, 1, ..., N-1]`` and ``allocate`` pops from its
+  END, so the first id handed out is N-1; freed blocks are appended and are
+  therefore reused first;
+* ``allocate(n)`` with fewer than ``n`` free blocks raises and changes nothing
+  (all or nothing); each allocated block gets reference count 1;
+* ``free(ids)`` drops one reference per listed id; a block whose count
+  reaches 0 goes back on the free list; dropping a reference that does not
+  exist (count would go below 0) is a double free, detected BEFORE any count
+  changes, so a failing call leaves the state untouched;
+* ``copy_on_write(id)``: a block with exactly one owner is written in place
+  (same id back); a shared block gives the writer a fresh block (the caller
+  copies the data) and loses one reference; a block with no owner is an error;
+* sharing: the page describes shared prompt blocks but shows no method that
+  adds a reference; ``incref`` and ``fork`` (a child sequence that shares all
+  of its parent's blocks) are that missing step;
+* ``usage_ratio = 1 - free / num_blocks``;
+* looking up a token whose logical block has not been allocated raises
+  IndexError.
+"""
+
+
+class OutOfBlocks(RuntimeError):
+    """Fewer free blocks than requested."""
+
+
+class DoubleFree(RuntimeError):
+    """A reference was dropped from a block that holds none."""
+
+
+class AllocatorModel:
+    def __init__(self, num_blocks, block_size):
+        if num_blocks <= 0 or block_size <= 0:
+            raise ValueError("num_blocks and block_size must be positive")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free_blocks = list(range(num_blocks))
+        self.ref_count = [0] * num_blocks
+        self.seqs = {}          # seq id -> {"blocks": [...], "tokens": int}
+        self.next_seq = 0
+        self.cow_copies = 0
+
+    # ---- block level -------------------------------------------------------
+    def set_free_order(self, order):
+        """Replace the free list by ``order`` (pop from its end); only legal
+        while every block is free, and ``order`` must be a permutation."""
+        order = [int(x) for x in order]
+        if any(self.ref_count):
+            raise ValueError("set_free_order needs every block free")
+        if sorted(order) != list(range(self.num_blocks)):
+            raise ValueError("order must be a permutation of range(num_blocks)")
+        self.free_blocks = order
+
+    def allocate(self, n=1):
+        if n < 0:
+            raise ValueError("negative count")
+        if len(self.free_blocks) < n:
+            raise OutOfBlocks(f"need {n} blocks, {len(self.free_blocks)} free")
+        out = []
+        for _ in range(n):
+            b = self.free_blocks.pop()
+            self.ref_count[b] = 1
+            out.append(b)
+        return out
+
+    def _check_ids(self, ids):
+        for b in ids:
+            if not 0 <= b < self.num_blocks:
+                raise ValueError(f"block id {b} out of range")
+
+    def free(self, ids):
+        ids = [int(b) for b in ids]
+        self._check_ids(ids)
+        drop = {}
+        for b in ids:
+            drop[b] = drop.get(b, 0) + 1
+        for b, c in drop.items():
+            if self.ref_count[b] - c < 0:
+                raise DoubleFree(f"block {b} freed more often than referenced")
+        for b in ids:
+            self.ref_count[b] -= 1
+            if self.ref_count[b] == 0:
+                self.free_blocks.append(b)
+
+    def incref(self, ids):
+        ids = [int(b) for b in ids]
+        self._check_ids(ids)
+        for b in ids:
+            if self.ref_count[b] == 0:
+                raise ValueError(f"block {b} is not allocated")
+        for b in ids:
+            self.ref_count[b] += 1
+
+    def copy_on_write(self, block_id):
+        """Returns (id_to_write, copied)."""
+        self._check_ids([block_id])
+        rc = self.ref_count[block_id]
+        if rc == 0:
+            raise ValueError(f"block {block_id} is not allocated")
+        if rc == 1:
+            return block_id, False
+        new_id = self.allocate(1)[0]
+        self.ref_count[block_id] -= 1
+        self.cow_copies += 1
+        return new_id, True
+
+    def usage_ratio(self):
+        return 1.0 - len(self.free_blocks) / self.num_blocks
+
+    # ---- sequence level ----------------------------------------------------
+    def seq_create(self):
+        sid = self.next_seq
+        self.next_seq += 1
+        self.seqs[sid] = {"blocks": [], "tokens": 0}
+        return sid
+
+    def seq_fork(self, sid):
+        parent = self.seqs[sid]
+        self.incref(parent["blocks"])
+        cid = self.next_seq
+        self.next_seq += 1
+        self.seqs[cid] = {"blocks": list(parent["blocks"]),
+                          "tokens": parent["tokens"]}
+        return cid
+
+    def seq_append_tokens(self, sid, n):
+        """Append ``n`` tokens; returns (slots, cow_pairs).
+
+        A token that starts a new logical block takes a freshly allocated
+        block; a token that lands in a partly filled last block that other
+        sequences share first gets its own copy of that block (copy-on-write;
+        the (src, dst) pair is returned for the caller to copy the data).
+        All or nothing: if the free list cannot cover every block the call
+        needs, nothing changes.
+        """
+        seq = self.seqs[sid]
+        bs = self.block_size
+        tokens = seq["tokens"]
+        need = 0
+        if n > 0 and tokens % bs != 0 and self.ref_count[seq["blocks"][-1]] > 1:
+            need += 1
+        need += (tokens + n + bs - 1) // bs - (tokens + bs - 1) // bs
+        if need > len(self.free_blocks):
+            raise OutOfBlocks(f"need {need} blocks, {len(self.free_blocks)} free")
+        slots, cow = [], []
+        for _ in range(n):
+            off = tokens % bs
+            if off == 0:
+                seq["blocks"].append(self.allocate(1)[0])
+            else:
+                last = seq["blocks"][-1]
+                new, copied = self.copy_on_write(last)
+                if copied:
+                    seq["blocks"][-1] = new
+                    cow.append((last, new))
+            slots.append(seq["blocks"][-1] * bs + off)
+            tokens += 1
+        seq["tokens"] = tokens
+        return slots, cow
+
+    def seq_free(self, sid):
+        seq = self.seqs.pop(sid)
+        self.free(seq["blocks"])
+
+    def seq_physical_block(self, sid, token):
+        seq = self.seqs[sid]
+        idx = token // self.block_size
+        if token < 0 or idx >= len(seq["blocks"]):
+            raise IndexError(f"token {token}: block {idx} not allocated")
+        return seq["blocks"][idx]
+
+    def export_block_tables(self, sids, max_blocks, pad=-1):
+        tables, lens = [], []
+        for sid in sids:
+            seq = self.seqs[sid]
+            if len(seq["blocks"]) > max_blocks:
+                raise ValueError("max_blocks smaller than a sequence's table")
+            tables.append(seq["blocks"] + [pad] * (max_blocks - len(seq["blocks"])))
+            lens.append(seq["tokens"])
+        return tables, lens
