@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of paged attention on one MI355X.
+
+A step is the whole hot path over one batch: the cache write of each
+sequence's newest token (reshape_and_cache), then paged-attention decode over
+contexts that include it.  Inputs are synthetic, drawn by the seeded workload
+generator, and resident in HBM before the timed region starts.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--partition 0]
+
+prints ONE JSON line.  ``value`` is context tokens attended per second over the
+timed steps (sum of context lengths per step x steps / wall time between two
+device synchronisations).  ``roofline`` reports the decode call (the dominant
+kernel) against HBM bandwidth: algorithmic bytes per call (K and V of every
+context token read once, each shared block counted once, plus Q, the output,
+the block-table entries, the lengths and int8 scales) over its average
+duration from HIP events on the launch stream.  ``cpu_baseline`` times the CPU
+oracle (test infrastructure, fp64 NumPy) on a bounded sample of the same
+workload on this host.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention: context tokens attended/s and achieved HBM GB/s (% of peak)"
+HBM_PEAK_GBPS = 8000.0
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+KERNEL_SOURCES = ["decode_kernel.h", "decode_dispatch.h", "decode.hip", "decode_f32.hip",
+                  "decode_f16.hip", "decode_bf16.hip", "decode_i8.hip"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_379_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl):
+    """Bytes the decode must move: every (block, kv head) row slice of a valid
+    token once (shared blocks once), int8 scales per used block, the table
+    entries and lengths it reads, Q in and the output out."""
+    bs = wl.block_size
+    row = wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_fmt]   # one token, all kv heads
+    valid = {}
+    table_entries = 0
+    for s in range(wl.num_seqs):
+        n = int(wl.context_lens[s])
+        nb = (n + bs - 1) // bs
+        table_entries += nb
+        for j in range(nb):
+            b = int(wl.block_tables[s, j])
+            valid[b] = max(valid.get(b, 0), min(bs, n - j * bs))
+    unique_tokens = sum(valid.values())
+    logical_tokens = int(wl.context_lens.sum())
+    kv = 2 * unique_tokens * row
+    scales = 2 * 4 * wl.num_kv_heads * len(valid) if wl.kv_fmt == "i8" else 0
+    qo = 2 * wl.num_seqs * wl.num_heads * wl.head_dim * ELEM_BYTES[wl.q_fmt]
+    meta = 4 * table_entries + 4 * wl.num_seqs
+    return dict(total=kv + scales + qo + meta, kv=kv, unique_tokens=unique_tokens,
+                logical_tokens=logical_tokens, logical_kv=2 * logical_tokens * row,
+                per_token=2 * row)
+
+
+def load_traffic(workload, ws):
+    """HBM bytes per decode call from committed rocprofv3 counter runs, if they
+    were taken on the kernel as it is now; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash() or rec.get("partition_size") != ws:
+        return None
+    return rec.get("bytes_per_call")
+
+
+def cpu_baseline(wl, budget_s):
+    """The oracle (never tuned) on the first sequences of the same workload,
+    cache write + decode, until ``budget_s`` of CPU time is spent."""
+    import contextlib
+    import oracle.paged_attention as pa
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    limiter = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
+    kc, vc = wl.key_cache, wl.value_cache
+    done, tokens, spent = 0, 0, 0.0
+    with limiter:
+        while done < wl.num_seqs and spent < budget_s:
+            s = done
+            t0 = time.perf_counter()
+            kc, vc = pa.reshape_and_cache(wl.k_new[s:s + 1], wl.v_new[s:s + 1], wl.new_fmt, kc, vc,
+                                          wl.kv_fmt, wl.slot_mapping[s:s + 1], wl.block_size,
+                                          wl.k_scales, wl.v_scales, in_place=True)
+            pa.paged_decode(wl.q[s:s + 1], wl.q_fmt, kc, vc, wl.kv_fmt, wl.block_tables[s:s + 1],
+                            wl.context_lens[s:s + 1], wl.block_size, wl.scale, wl.k_scales,
+                            wl.v_scales)
+            spent += time.perf_counter() - t0
+            tokens += int(wl.context_lens[s])
+            done += 1
+    return {"value": tokens / spent, "unit": "context tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {done} of {wl.num_seqs} sequences ({tokens} context tokens), "
+                      f"cache write + decode, fp64 NumPy, BLAS threads limited to {cores}",
+            "seconds": round(spent, 3)}
+
+
+def parity_sample(wl, out, n=4, seed=0):
+    import oracle.paged_attention as pa
+    rng = np.random.default_rng(seed)
+    seqs = np.sort(rng.choice(wl.num_seqs, size=min(n, wl.num_seqs), replace=False))
+    ref = pa.paged_decode(wl.q[seqs], wl.q_fmt, wl.key_cache, wl.value_cache, wl.kv_fmt,
+                          wl.block_tables[seqs], wl.context_lens[seqs], wl.block_size, wl.scale,
+                          wl.k_scales, wl.v_scales)
+    got = out.float().cpu().numpy().astype(np.float64)[seqs]
+    return float(np.abs(got - ref).max()), seqs.tolist()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 70B-shaped fp16)")
+    ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = library default)")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: the decode path runs on one GPU; the multi-GPU layout (sequences or kv "
+              "heads per GPU, no collective inside attention) is not built here; use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_379_amd as pkv
+    from paged_kv_cache_379_amd import workloads as W
+
+    pkv.load()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    t = time.perf_counter()
+    wl = W.make_workload(args.config, seed=args.seed)
+    log(f"workload {wl.name}: {wl.num_seqs} seqs, {wl.num_heads}/{wl.num_kv_heads} heads, "
+        f"D={wl.head_dim}, {wl.kv_fmt} KV, sum ctx {int(wl.context_lens.sum())} "
+        f"(drawn in {time.perf_counter() - t:.1f}s)")
+
+    def up(arr, fmt):
+        arr = np.ascontiguousarray(arr)
+        if fmt == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(arr).to(dev)
+
+    q = up(wl.q, wl.q_fmt)
+    kc, vc = up(wl.key_cache, wl.kv_fmt), up(wl.value_cache, wl.kv_fmt)
+    tables, lens = up(wl.block_tables, "i32"), up(wl.context_lens, "i32")
+    k_new, v_new = up(wl.k_new, wl.new_fmt), up(wl.v_new, wl.new_fmt)
+    slots = up(wl.slot_mapping, "i32")
+    ks = up(wl.k_scales, "f32") if wl.kv_fmt == "i8" else None
+    vs = up(wl.v_scales, "f32") if wl.kv_fmt == "i8" else None
+    out = torch.empty_like(q)
+    B, H, D = q.shape
+    MB = tables.shape[1]
+    part = pkv.decode_partition_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition)
+    need = pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def write():
+        pkv.reshape_and_cache(k_new, v_new, kc, vc, slots, ks, vs)
+
+    def decode():
+        pkv.paged_attention_decode(out, q, kc, vc, tables, lens, wl.block_size, wl.scale, ks, vs,
+                                   partition_size=args.partition, workspace=ws)
+
+    for _ in range(args.warmup):
+        write()
+        decode()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record()
+        write()
+        ev[i][1].record()
+        decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    write_us = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) * 1e3
+    decode_us = float(np.mean([b.elapsed_time(c) for _, b, c in ev])) * 1e3
+    log(f"timed {args.steps} steps in {elapsed * 1e3:.2f} ms; decode {decode_us:.1f} us, "
+        f"cache write {write_us:.1f} us")
+
+    # Reference point: the library's own streaming copy of 1 GiB.
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    pkv.stream_copy(dst, src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        pkv.stream_copy(dst, src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+
+    ab = algorithmic_bytes(wl)
+    ctx_per_step = ab["logical_tokens"]
+    value = ctx_per_step * args.steps / elapsed
+    achieved = ab["total"] / (decode_us * 1e-6) / 1e9
+    traffic = load_traffic(wl.name, part)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "num_seqs": wl.num_seqs, "num_heads": wl.num_heads, "num_kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim, "block_size": wl.block_size, "kv_dtype": wl.kv_fmt,
+            "q_dtype": wl.q_fmt, "sum_context_tokens": ctx_per_step,
+            "max_blocks_per_seq": MB, "num_blocks": wl.num_blocks,
+            "partition_tokens": part, "seed": wl.seed,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "kernel": "paged_decode_kernel" + ("+reduce" if part else ""),
+            "bytes_per_call": ab["total"], "decode_us": decode_us,
+        },
+        "decode_tokens_per_s": ctx_per_step / (decode_us * 1e-6),
+        "cache_write_us": write_us,
+        "copy_probe_gbps": copy_gbps,
+        "decode_frac_of_copy_probe": achieved / copy_gbps,
+        "kernel_hash": kernel_hash(),
+    }
+    if ab["unique_tokens"] != ab["logical_tokens"]:
+        result["roofline"]["logical_bytes_per_call"] = ab["total"] - ab["kv"] + ab["logical_kv"]
+        result["roofline"]["logical_gbps"] = (ab["total"] - ab["kv"] + ab["logical_kv"]) / (decode_us * 1e-6) / 1e9
+    if not args.no_parity:
+        # one more step, then compare sampled sequences with the oracle
+        write()
+        decode()
+        torch.cuda.synchronize()
+        import oracle.paged_attention as pa
+        pa.reshape_and_cache(wl.k_new, wl.v_new, wl.new_fmt, wl.key_cache, wl.value_cache,
+                             wl.kv_fmt, wl.slot_mapping, wl.block_size, wl.k_scales, wl.v_scales,
+                             in_place=True)
+        err, seqs = parity_sample(wl, out)
+        tol = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-3, "i8": 2e-2}[wl.kv_fmt]
+        result["parity"] = {"max_abs_err": err, "tol": tol, "seqs": seqs, "ok": err <= tol}
+        log(f"parity on seqs {seqs}: max abs err {err:.3g} (tol {tol:g})")
+        # the oracle leg below reads the caches as written (idempotent rewrite)
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle for about {args.cpu_budget:.0f}s")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

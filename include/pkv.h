@@ -1,0 +1,280 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged-attention decode on AMD MI355X (gfx950).
+ *
+ * Page keys used in the citations below:
+ *   [P1] "大模型KV Cache内存优化与PagedAttention显存管理机制详解" (yunthe.com)
+ *   [P2] "大模型部署中KV Cache优化策略与显存管理实践教程" (yunthe.com)
+ *   [P3] "vLLM推理框架源码初探：PagedAttention的显存管理设计" (trdm.cn)
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns an int status (PKV_OK = 0) and never lets a C++
+ *     exception cross the ABI.  On failure pkv_last_error() returns a message
+ *     for the calling thread, valid until that thread's next pkv_* call.
+ *   - Device buffers are owned by the caller (the library never allocates,
+ *     frees or synchronises device memory, except that pkv_copy_blocks takes
+ *     its pairs from host memory).  Host buffers are only read or written during
+ *     the call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Kernels are enqueued on it; functions return before they finish.
+ *   - Shapes and sizes are validated on the host.  Values that live in device
+ *     memory (block tables, context lengths, slots) cannot be checked without a
+ *     device sync: kernels clamp them so that no access leaves its buffer, and
+ *     pkv_validate_tables checks host copies when the caller wants an error.
+ *
+ * Data layout (device, row-major, from the address formula in the kernel
+ * sketch of [P1] "PagedAttention注意力计算流程"):
+ *   key_cache, value_cache  [num_blocks][block_size][num_kv_heads][head_dim]
+ *                           element (b, o, h, d) at ((b*bs + o)*Hkv + h)*D + d
+ *   q, out                  [num_seqs][num_heads][head_dim]
+ *   block_tables            int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens            int32 [num_seqs]
+ *   k_scales, v_scales      fp32 [num_blocks][num_kv_heads]   (int8 caches)
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,  /* null pointer, bad shape, bad enum value        */
+  PKV_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, format)   */
+  PKV_ERR_OOM = 3,          /* allocator: not enough free blocks              */
+  PKV_ERR_DOUBLE_FREE = 4,  /* allocator: a reference dropped twice           */
+  PKV_ERR_INDEX = 5,        /* allocator: token past the allocated blocks     */
+  PKV_ERR_HIP = 6,          /* a HIP runtime call failed                      */
+  PKV_ERR_WORKSPACE = 7     /* decode: workspace missing or too small         */
+};
+
+/* Storage formats. */
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 };
+
+/* Message describing the calling thread's last failure ("" if none). */
+const char* pkv_last_error(void);
+
+/* ABI version (bumped when a signature changes). */
+int pkv_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Decode                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Tokens per context partition that pkv_paged_attention_decode will use for
+ * these shapes when called with the same `partition_size` (0 = automatic).
+ * The result is a multiple of block_size, or 0 if the context is not split.
+ * Returns 0 for invalid shapes.
+ */
+int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
+                              int head_dim, int block_size,
+                              int max_blocks_per_seq, int partition_size);
+
+/*
+ * Workspace bytes the decode needs for these shapes (0 when the context is
+ * not split, in which case `workspace` may be NULL).  Same arguments as
+ * pkv_decode_partition_size.
+ */
+size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                 int head_dim, int block_size,
+                                 int max_blocks_per_seq, int partition_size);
+
+/*
+ * Paged-attention decode ([P1] "PagedAttention注意力计算流程" and its kernel
+ * sketch; [P3] section 三): for each sequence s and query head h, with
+ * n = context_lens[s] and kv head kvh = h / (num_heads / num_kv_heads),
+ *
+ *   token i < n  ->  physical block block_tables[s][i / bs], offset i % bs
+ *   score_i      =   scale * dot(q[s][h], K[i][kvh])
+ *   out[s][h]    =   sum_i softmax(score)_i * V[i][kvh]
+ *
+ * with K/V of an int8 cache dequantised as code * scale[block][kvh]
+ * ([P2] "量化压缩KV Cache的INT8与FP8方案"; one scale per (block, kv head)).
+ * The softmax is computed stably (scores shifted by their maximum), in fp32;
+ * long contexts are split into partitions whose partial results are merged
+ * exactly.  n = 0 gives an all-zero output.  Table entries past
+ * ceil(n / bs) and slots past n are never read.
+ *
+ *   out          device, [B][H][D] in q_dtype (written)
+ *   q            device, [B][H][D] in q_dtype: F32, F16 or BF16
+ *   key_cache    device, see layout above, kv_dtype
+ *   value_cache  device, same shape and format as key_cache
+ *   k_scales     device fp32 [NB][Hkv], required iff kv_dtype == PKV_I8
+ *   v_scales     device fp32 [NB][Hkv], required iff kv_dtype == PKV_I8
+ *   block_tables device int32 [B][max_blocks_per_seq]
+ *   context_lens device int32 [B]; values are clamped to
+ *                [0, max_blocks_per_seq * block_size]
+ *   kv_dtype     F32 (q F32), F16 (q F16), BF16 (q BF16), I8 (q F16 or BF16)
+ *   head_dim     64 or 128; block_size 16; num_heads / num_kv_heads in
+ *                {1, 2, 4, 8, 16}
+ *   partition_size  tokens per partition, a multiple of block_size, or 0 for
+ *                the library's choice; a value >= the longest possible context
+ *                disables splitting
+ *   workspace    device scratch of >= pkv_decode_workspace_size(...) bytes
+ *                (may be NULL when that is 0); fully rewritten by each call,
+ *                so calls that share a workspace must be stream-ordered
+ *
+ * A block id outside [0, num_blocks) in a position that is read makes that
+ * block's tokens count as masked (output unspecified but finite, no
+ * out-of-bounds access).  Errors: INVALID_ARG (null pointer, bad shape or
+ * format pair), UNSUPPORTED (head_dim, block_size, group size), WORKSPACE,
+ * HIP (launch failure).
+ */
+int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
+                               const void* value_cache, const float* k_scales,
+                               const float* v_scales, const int32_t* block_tables,
+                               const int32_t* context_lens, int num_seqs,
+                               int num_heads, int num_kv_heads, int head_dim,
+                               int block_size, int max_blocks_per_seq,
+                               int num_blocks, float scale, int q_dtype,
+                               int kv_dtype, int partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Cache write                                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * reshape_and_cache: scatter each new token's K and V rows into its cache
+ * slot.  Token t goes to block slot_mapping[t] / bs, offset slot_mapping[t] % bs
+ * (the inverse of the physical offset phys * bs + offset of the [P1] kernel
+ * sketch).  A slot < 0, or one at or past num_blocks * bs, is skipped.
+ *
+ *   k, v         device, [num_tokens][num_kv_heads][head_dim] in src_dtype
+ *   key_cache, value_cache  device, layout above, kv_dtype (written)
+ *   k_scales, v_scales      device fp32 [NB][Hkv], required iff kv_dtype == I8:
+ *                the existing scale of each (block, kv head); the int8 code is
+ *                clamp(rint(x / scale), -127, 127) with the division and the
+ *                round-half-to-even done in fp32
+ *   slot_mapping device int32 [num_tokens]
+ *   src_dtype    equal to kv_dtype for float caches; F32, F16 or BF16 for I8
+ *
+ * Slots must be distinct among the tokens of one call (else which write wins
+ * is unspecified).  Errors: INVALID_ARG, UNSUPPORTED, HIP.
+ */
+int pkv_reshape_and_cache(const void* k, const void* v, void* key_cache,
+                          void* value_cache, const float* k_scales,
+                          const float* v_scales, const int32_t* slot_mapping,
+                          int num_tokens, int num_kv_heads, int head_dim,
+                          int block_size, int num_blocks, int src_dtype,
+                          int kv_dtype, void* stream);
+
+/*
+ * Copy whole physical blocks (K and V, and for int8 caches their scales) from
+ * src to dst: the data copy that copy-on-write leaves to the caller ([P3]
+ * section 二, copy_on_write).  `pairs` is HOST memory: n_pairs (src, dst)
+ * int32 pairs; ids must be in [0, num_blocks) and dst ids distinct and not
+ * used as a src in the same call.  block_bytes = bs * Hkv * D * element size.
+ * k_scales / v_scales may be NULL (float caches); scale_stride = Hkv.
+ * Errors: INVALID_ARG, HIP.
+ */
+int pkv_copy_blocks(void* key_cache, void* value_cache, float* k_scales,
+                    float* v_scales, const int32_t* pairs, int n_pairs,
+                    size_t block_bytes, int num_blocks, int scale_stride,
+                    void* stream);
+
+/*
+ * Plain device-to-device streaming copy of `bytes` bytes (a multiple of 16,
+ * 16-byte aligned pointers) with the library's own kernel: the reference
+ * point for achievable HBM bandwidth and for scaling hardware byte counters.
+ */
+int pkv_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator ([P3] section 二: BlockManager / BlockTable; [P1]     */
+/* "PagedAttention分页内存管理原理" and "vLLM调度器与PagedAttention协同工作"). */
+/* Host memory only, no device calls.  Not thread safe: one allocator must   */
+/* not be used from two threads at once.                                    */
+/* ------------------------------------------------------------------------ */
+
+typedef struct pkv_allocator pkv_allocator;
+
+/* A pool of num_blocks blocks of block_size tokens; free list = 0..N-1, and
+ * blocks leave from its END (the first allocation returns N-1). */
+int pkv_allocator_create(int num_blocks, int block_size, pkv_allocator** out);
+int pkv_allocator_destroy(pkv_allocator* a);
+
+/* Replace the free list by `order` (n == num_blocks, a permutation); legal
+ * only while every block is free.  Blocks then leave from order[n-1] down. */
+int pkv_allocator_set_free_order(pkv_allocator* a, const int32_t* order, int n);
+
+/* Allocate n blocks (all or nothing; OOM leaves the state unchanged); each
+ * gets reference count 1.  out_ids: host int32[n]. */
+int pkv_allocate(pkv_allocator* a, int n, int32_t* out_ids);
+
+/* Drop one reference per listed id; a block reaching 0 goes back on the free
+ * list (reused first).  A drop below 0 is DOUBLE_FREE, detected before any
+ * change. */
+int pkv_free(pkv_allocator* a, const int32_t* ids, int n);
+
+/* Add one reference per listed id (ids must be allocated): sharing of prompt
+ * blocks ([P1] shared prefixes through reference counts). */
+int pkv_incref(pkv_allocator* a, const int32_t* ids, int n);
+
+/* Copy-on-write of one block ([P3] section 二): a sole owner keeps the block
+ * (*copied = 0); a shared block gives the writer a new block (*copied = 1,
+ * the caller copies the data) and drops one reference of the old one.
+ * INVALID_ARG if the block is not allocated; OOM if no block is free. */
+int pkv_copy_on_write(pkv_allocator* a, int32_t id, int32_t* new_id, int* copied);
+
+int pkv_ref_count(const pkv_allocator* a, int32_t id, int* out);
+int pkv_num_free(const pkv_allocator* a, int* out);
+/* 1 - free / num_blocks ([P3] section 二, usage_ratio). */
+int pkv_usage_ratio(const pkv_allocator* a, double* out);
+/* Copy of the free list, bottom to top (the next block to leave is last). */
+int pkv_free_list(const pkv_allocator* a, int32_t* out, int cap, int* n);
+/* Number of copy-on-write copies handed out so far. */
+int pkv_cow_count(const pkv_allocator* a, int64_t* out);
+
+/* Sequences: a logical block table plus a token count ([P3] BlockTable). */
+int pkv_seq_create(pkv_allocator* a, int32_t* seq);
+/* A child sequence sharing all of the parent's blocks (one more reference
+ * each) and its token count: parallel sampling / shared prompts. */
+int pkv_seq_fork(pkv_allocator* a, int32_t seq, int32_t* child);
+/*
+ * Append n tokens with on-demand allocation ([P1] scheduler section): a token
+ * that starts a logical block takes a new block; a token that lands in a
+ * partly filled last block shared with other sequences first triggers
+ * copy-on-write of that block.  All or nothing (OOM leaves the state
+ * unchanged).  slots_out: host int32[n], slot = block * bs + offset of each
+ * token.  cow_pairs_out: host int32[2 * cow_cap] receiving (src, dst) block
+ * pairs to copy before writing (at most 1 per call); *n_cow their number.
+ */
+int pkv_seq_append_tokens(pkv_allocator* a, int32_t seq, int n, int32_t* slots_out,
+                          int32_t* cow_pairs_out, int cow_cap, int* n_cow);
+/* Release all of the sequence's block references and forget it. */
+int pkv_seq_free(pkv_allocator* a, int32_t seq);
+int pkv_seq_num_tokens(const pkv_allocator* a, int32_t seq, int* out);
+int pkv_seq_block_ids(const pkv_allocator* a, int32_t seq, int32_t* out, int cap, int* n);
+/* Physical block of a logical token ([P3] BlockTable lookup): INDEX if the
+ * token's logical block has not been allocated. */
+int pkv_seq_physical_block(const pkv_allocator* a, int32_t seq, int token, int32_t* out);
+/*
+ * Export host block tables for a batch: out_tables int32[n][max_blocks]
+ * padded with `pad`, out_lens int32[n] token counts.  INVALID_ARG if a
+ * sequence holds more than max_blocks blocks.
+ */
+int pkv_export_block_tables(const pkv_allocator* a, const int32_t* seqs, int n,
+                            int max_blocks, int32_t pad, int32_t* out_tables,
+                            int32_t* out_lens);
+
+/*
+ * Debug check of HOST copies of decode inputs: every table entry a context
+ * reads lies in [0, num_blocks), and 0 <= len <= max_blocks * block_size.
+ * On INVALID_ARG, *bad_seq / *bad_block name the first offending entry
+ * (bad_block = -1 for a bad length).
+ */
+int pkv_validate_tables(const int32_t* tables, const int32_t* lens, int num_seqs,
+                        int max_blocks, int block_size, int num_blocks,
+                        int* bad_seq, int* bad_block);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* PKV_H_ */

@@ -1,0 +1,379 @@
+"""Paged-attention decode for AMD MI355X (gfx950): Python binding of libpkv.so.
+
+The binding only marshals arguments: torch tensors supply device memory and
+the current HIP stream, every step of the computation runs in the library's
+HIP kernels, and there is no CPU fallback.  If libpkv.so is missing the first
+call raises; build it with ``python -m paged_kv_cache_379_amd.build``.
+
+The host-side block allocator (:class:`BlockAllocator`) runs in the same
+library and needs no GPU.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "load", "LIB_PATH", "PkvError", "OutOfBlocks", "DoubleFree",
+    "paged_attention_decode", "decode_workspace_size", "decode_partition_size",
+    "reshape_and_cache", "copy_blocks", "stream_copy", "validate_tables",
+    "BlockAllocator", "F32", "F16", "BF16", "I8",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+# Status codes and formats (include/pkv.h).
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OOM, ERR_DOUBLE_FREE, ERR_INDEX, ERR_HIP, ERR_WORKSPACE = range(8)
+F32, F16, BF16, I8 = 0, 1, 2, 3
+
+
+class PkvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"pkv error {code}: {msg}")
+        self.code = code
+
+
+class OutOfBlocks(PkvError):
+    """Not enough free blocks (the allocator state is unchanged)."""
+
+
+class DoubleFree(PkvError):
+    """A block reference was dropped more often than it was taken."""
+
+
+_lib = None
+
+_c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_SIGS = {
+    "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_abi_version": (_c_int, []),
+    "pkv_decode_partition_size": (_c_int, [_c_int] * 7),
+    "pkv_decode_workspace_size": (_c_size, [_c_int] * 7),
+    "pkv_paged_attention_decode": (_c_int, [_vp] * 8 + [_c_int] * 7 + [ctypes.c_float] + [_c_int] * 3
+                                   + [_vp, _c_size, _vp]),
+    "pkv_reshape_and_cache": (_c_int, [_vp] * 7 + [_c_int] * 6 + [_vp]),
+    "pkv_copy_blocks": (_c_int, [_vp] * 4 + [_i32p, _c_int, _c_size, _c_int, _c_int, _vp]),
+    "pkv_stream_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
+    "pkv_allocator_create": (_c_int, [_c_int, _c_int, ctypes.POINTER(_vp)]),
+    "pkv_allocator_destroy": (_c_int, [_vp]),
+    "pkv_allocator_set_free_order": (_c_int, [_vp, _i32p, _c_int]),
+    "pkv_allocate": (_c_int, [_vp, _c_int, _i32p]),
+    "pkv_free": (_c_int, [_vp, _i32p, _c_int]),
+    "pkv_incref": (_c_int, [_vp, _i32p, _c_int]),
+    "pkv_copy_on_write": (_c_int, [_vp, ctypes.c_int32, _i32p, ctypes.POINTER(_c_int)]),
+    "pkv_ref_count": (_c_int, [_vp, ctypes.c_int32, ctypes.POINTER(_c_int)]),
+    "pkv_num_free": (_c_int, [_vp, ctypes.POINTER(_c_int)]),
+    "pkv_usage_ratio": (_c_int, [_vp, ctypes.POINTER(ctypes.c_double)]),
+    "pkv_free_list": (_c_int, [_vp, _i32p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_cow_count": (_c_int, [_vp, ctypes.POINTER(ctypes.c_int64)]),
+    "pkv_seq_create": (_c_int, [_vp, _i32p]),
+    "pkv_seq_fork": (_c_int, [_vp, ctypes.c_int32, _i32p]),
+    "pkv_seq_append_tokens": (_c_int, [_vp, ctypes.c_int32, _c_int, _i32p, _i32p, _c_int,
+                                       ctypes.POINTER(_c_int)]),
+    "pkv_seq_free": (_c_int, [_vp, ctypes.c_int32]),
+    "pkv_seq_num_tokens": (_c_int, [_vp, ctypes.c_int32, ctypes.POINTER(_c_int)]),
+    "pkv_seq_block_ids": (_c_int, [_vp, ctypes.c_int32, _i32p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_seq_physical_block": (_c_int, [_vp, ctypes.c_int32, _c_int, _i32p]),
+    "pkv_export_block_tables": (_c_int, [_vp, _i32p, _c_int, _c_int, ctypes.c_int32, _i32p, _i32p]),
+    "pkv_validate_tables": (_c_int, [_i32p, _i32p, _c_int, _c_int, _c_int, _c_int,
+                                     ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def load(path=None):
+    """Load libpkv.so (once) and return the ctypes handle; raises if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"libpkv.so not found at {path}: run "
+                           "`python -m paged_kv_cache_379_amd.build` first")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc == OK:
+        return
+    msg = _lib.pkv_last_error().decode(errors="replace")
+    if rc == ERR_OOM:
+        raise OutOfBlocks(rc, msg)
+    if rc == ERR_DOUBLE_FREE:
+        raise DoubleFree(rc, msg)
+    if rc == ERR_INDEX:
+        raise IndexError(msg)
+    if rc == ERR_INVALID_ARG:
+        raise ValueError(msg)
+    raise PkvError(rc, msg)
+
+
+# ---------------------------------------------------------------------------
+# Device entry points (torch tensors in, nothing computed here).
+
+def _torch():
+    import torch
+    return torch
+
+
+def _fmt(t):
+    torch = _torch()
+    return {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8}[t.dtype]
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, partition_size=0):
+    return load().pkv_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                            block_size, max_blocks_per_seq, partition_size)
+
+
+def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, partition_size=0):
+    return load().pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                            block_size, max_blocks_per_seq, partition_size)
+
+
+def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens,
+                           block_size, scale, k_scales=None, v_scales=None,
+                           partition_size=0, workspace=None, stream=None):
+    """Decode attention over a paged KV cache (see include/pkv.h).
+
+    out, q [B, H, D]; key_cache, value_cache [NB, block_size, Hkv, D];
+    block_tables int32 [B, MB]; context_lens int32 [B]; k/v_scales fp32
+    [NB, Hkv] for int8 caches.  A workspace of the needed size is allocated
+    from torch when none is given.
+    """
+    torch = _torch()
+    lib = load()
+    B, H, D = q.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    if D2 != D or bs != block_size or tuple(out.shape) != (B, H, D) or out.dtype != q.dtype:
+        raise ValueError("shape or dtype mismatch between q, out and the caches")
+    if tuple(value_cache.shape) != tuple(key_cache.shape) or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    MB = block_tables.shape[1]
+    need = lib.pkv_decode_workspace_size(B, H, Hkv, D, bs, MB, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.pkv_paged_attention_decode(
+        _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(key_cache, "key_cache"),
+        _dev_ptr(value_cache, "value_cache"), _dev_ptr(k_scales, "k_scales", torch.float32),
+        _dev_ptr(v_scales, "v_scales", torch.float32),
+        _dev_ptr(block_tables, "block_tables", torch.int32),
+        _dev_ptr(context_lens, "context_lens", torch.int32),
+        B, H, Hkv, D, bs, MB, NB, float(scale), _fmt(q), _fmt(key_cache), int(partition_size),
+        _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(rc)
+    return out
+
+
+def reshape_and_cache(k, v, key_cache, value_cache, slot_mapping, k_scales=None,
+                      v_scales=None, stream=None):
+    """Write new tokens' K/V rows [T, Hkv, D] into their slots (see include/pkv.h)."""
+    torch = _torch()
+    lib = load()
+    T, Hkv, D = k.shape
+    NB, bs, Hkv2, D2 = key_cache.shape
+    if (Hkv2, D2) != (Hkv, D) or tuple(v.shape) != tuple(k.shape) or slot_mapping.shape != (T,):
+        raise ValueError("shape mismatch")
+    rc = lib.pkv_reshape_and_cache(
+        _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(key_cache, "key_cache"),
+        _dev_ptr(value_cache, "value_cache"), _dev_ptr(k_scales, "k_scales", torch.float32),
+        _dev_ptr(v_scales, "v_scales", torch.float32),
+        _dev_ptr(slot_mapping, "slot_mapping", torch.int32),
+        T, Hkv, D, bs, NB, _fmt(k), _fmt(key_cache), _stream(stream))
+    _check(rc)
+
+
+def copy_blocks(key_cache, value_cache, pairs, k_scales=None, v_scales=None, stream=None):
+    """Copy whole blocks src -> dst for each (src, dst) in ``pairs`` (host ints)."""
+    lib = load()
+    arr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    NB = key_cache.shape[0]
+    block_bytes = key_cache[0].numel() * key_cache.element_size()
+    rc = lib.pkv_copy_blocks(
+        _dev_ptr(key_cache, "key_cache"), _dev_ptr(value_cache, "value_cache"),
+        _dev_ptr(k_scales, "k_scales"), _dev_ptr(v_scales, "v_scales"),
+        arr.ctypes.data_as(_i32p), len(arr), block_bytes, NB,
+        key_cache.shape[2], _stream(stream))
+    _check(rc)
+
+
+def stream_copy(dst, src, nbytes=None, stream=None):
+    """The library's streaming copy kernel (bandwidth reference)."""
+    lib = load()
+    nbytes = nbytes if nbytes is not None else src.numel() * src.element_size()
+    _check(lib.pkv_stream_copy(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), nbytes, _stream(stream)))
+
+
+def validate_tables(tables, lens, block_size, num_blocks):
+    """Host check of decode tables; returns None or (bad_seq, bad_block)."""
+    lib = load()
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    l = np.ascontiguousarray(lens, dtype=np.int32)
+    bs_, bb = ctypes.c_int(), ctypes.c_int()
+    rc = lib.pkv_validate_tables(t.ctypes.data_as(_i32p), l.ctypes.data_as(_i32p), t.shape[0],
+                                 t.shape[1], block_size, num_blocks, ctypes.byref(bs_), ctypes.byref(bb))
+    if rc == OK:
+        return None
+    if rc == ERR_INVALID_ARG and bs_.value >= 0:
+        return (bs_.value, bb.value)
+    _check(rc)
+
+
+# ---------------------------------------------------------------------------
+# Host block allocator.
+
+def _i32(a):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32).reshape(-1))
+    return arr, arr.ctypes.data_as(_i32p)
+
+
+class BlockAllocator:
+    """Ref-counted free-list allocator with copy-on-write (host only)."""
+
+    def __init__(self, num_blocks, block_size):
+        self._lib = load()
+        h = _vp()
+        _check(self._lib.pkv_allocator_create(num_blocks, block_size, ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def set_free_order(self, order):
+        arr, p = _i32(order)
+        _check(self._lib.pkv_allocator_set_free_order(self._h, p, len(arr)))
+
+    def allocate(self, n=1):
+        out = np.empty(n, dtype=np.int32)
+        _check(self._lib.pkv_allocate(self._h, n, out.ctypes.data_as(_i32p)))
+        return out.tolist()
+
+    def free(self, ids):
+        arr, p = _i32(ids)
+        _check(self._lib.pkv_free(self._h, p, len(arr)))
+
+    def incref(self, ids):
+        arr, p = _i32(ids)
+        _check(self._lib.pkv_incref(self._h, p, len(arr)))
+
+    def copy_on_write(self, block_id):
+        new, copied = ctypes.c_int32(), ctypes.c_int()
+        _check(self._lib.pkv_copy_on_write(self._h, block_id, ctypes.byref(new), ctypes.byref(copied)))
+        return new.value, bool(copied.value)
+
+    def ref_count(self, block_id):
+        out = ctypes.c_int()
+        _check(self._lib.pkv_ref_count(self._h, block_id, ctypes.byref(out)))
+        return out.value
+
+    def num_free(self):
+        out = ctypes.c_int()
+        _check(self._lib.pkv_num_free(self._h, ctypes.byref(out)))
+        return out.value
+
+    def usage_ratio(self):
+        out = ctypes.c_double()
+        _check(self._lib.pkv_usage_ratio(self._h, ctypes.byref(out)))
+        return out.value
+
+    def free_list(self):
+        out = np.empty(self.num_blocks, dtype=np.int32)
+        n = ctypes.c_int()
+        _check(self._lib.pkv_free_list(self._h, out.ctypes.data_as(_i32p), self.num_blocks,
+                                       ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def cow_count(self):
+        out = ctypes.c_int64()
+        _check(self._lib.pkv_cow_count(self._h, ctypes.byref(out)))
+        return out.value
+
+    def seq_create(self):
+        out = ctypes.c_int32()
+        _check(self._lib.pkv_seq_create(self._h, ctypes.byref(out)))
+        return out.value
+
+    def seq_fork(self, seq):
+        out = ctypes.c_int32()
+        _check(self._lib.pkv_seq_fork(self._h, seq, ctypes.byref(out)))
+        return out.value
+
+    def seq_append_tokens(self, seq, n):
+        """Returns (slots, cow_pairs) like the allocator model."""
+        slots = np.empty(max(n, 1), dtype=np.int32)
+        cow = np.empty(2, dtype=np.int32)
+        ncow = ctypes.c_int()
+        _check(self._lib.pkv_seq_append_tokens(self._h, seq, n, slots.ctypes.data_as(_i32p),
+                                               cow.ctypes.data_as(_i32p), 1, ctypes.byref(ncow)))
+        pairs = [(int(cow[0]), int(cow[1]))] if ncow.value else []
+        return slots[:n].tolist(), pairs
+
+    def seq_free(self, seq):
+        _check(self._lib.pkv_seq_free(self._h, seq))
+
+    def seq_num_tokens(self, seq):
+        out = ctypes.c_int()
+        _check(self._lib.pkv_seq_num_tokens(self._h, seq, ctypes.byref(out)))
+        return out.value
+
+    def seq_block_ids(self, seq):
+        n = ctypes.c_int()
+        rc = self._lib.pkv_seq_block_ids(self._h, seq, None, 0, ctypes.byref(n))
+        if rc not in (OK, ERR_INVALID_ARG):
+            _check(rc)
+        out = np.empty(max(n.value, 1), dtype=np.int32)
+        _check(self._lib.pkv_seq_block_ids(self._h, seq, out.ctypes.data_as(_i32p), n.value,
+                                           ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def seq_physical_block(self, seq, token):
+        out = ctypes.c_int32()
+        _check(self._lib.pkv_seq_physical_block(self._h, seq, token, ctypes.byref(out)))
+        return out.value
+
+    def export_block_tables(self, seqs, max_blocks, pad=-1):
+        arr, p = _i32(seqs)
+        tables = np.empty((len(arr), max_blocks), dtype=np.int32)
+        lens = np.empty(len(arr), dtype=np.int32)
+        _check(self._lib.pkv_export_block_tables(self._h, p, len(arr), max_blocks, pad,
+                                                 tables.ctypes.data_as(_i32p),
+                                                 lens.ctypes.data_as(_i32p)))
+        return tables, lens

@@ -1,0 +1,269 @@
+// The cache write (reshape_and_cache), the block copy behind copy-on-write,
+// and a plain streaming copy used as the bandwidth reference.
+//
+// Page keys:
+//   [P1] "大模型KV Cache内存优化与PagedAttention显存管理机制详解" (yunthe.com)
+//   [P2] "大模型部署中KV Cache优化策略与显存管理实践教程" (yunthe.com)
+//   [P3] "vLLM推理框架源码初探：PagedAttention的显存管理设计" (trdm.cn)
+//
+// A new token's K and V rows ([Hkv][D], contiguous in the source and in the
+// cache slot, by the layout of the [P1] kernel sketch) are written to
+// block slot / bs, offset slot % bs.  One workgroup per (token, K or V) moves
+// the row with 16-byte loads and stores; an int8 cache quantises on the way
+// with the (block, kv head) scale ([P2] INT8 KV cache section; scale
+// granularity is this library's reading).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <vector>
+
+#include "decode_kernel.h"
+#include "pkv_internal.h"
+
+namespace {
+
+using pkv_dev::Format;
+using pkv_dev::unpack16;
+
+struct CacheWriteArgs {
+  const uint8_t* k;
+  const uint8_t* v;
+  uint8_t* key_cache;
+  uint8_t* value_cache;
+  const float* k_scales;
+  const float* v_scales;
+  const int32_t* slots;
+  int64_t num_slots;  // num_blocks * block_size
+  int num_kv_heads;
+  int head_dim;
+  int block_size;
+};
+
+constexpr int kWriteThreads = 256;
+
+template <int SF, int KF>
+__global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(CacheWriteArgs a) {
+  const int t = blockIdx.x;
+  const bool is_v = blockIdx.y != 0;
+  const int slot = a.slots[t];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const uint8_t* src = is_v ? a.v : a.k;
+  uint8_t* dst = is_v ? a.value_cache : a.key_cache;
+  const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * a.head_dim;
+  if constexpr (KF != PKV_I8) {
+    static_assert(SF == KF, "float caches take rows of their own format");
+    const int64_t vecs = row_elems * Format<KF>::kBytes / 16;
+    const uint4* s4 = reinterpret_cast<const uint4*>(src) + t * vecs;
+    uint4* d4 = reinterpret_cast<uint4*>(dst) + static_cast<int64_t>(slot) * vecs;
+    for (int64_t c = threadIdx.x; c < vecs; c += kWriteThreads) d4[c] = s4[c];
+  } else {
+    const float* scales = is_v ? a.v_scales : a.k_scales;
+    const int blk = slot / a.block_size;
+    constexpr int kSrcVecs = 16 * Format<SF>::kBytes / 16;  // uint4s per 16 elements
+    const int64_t chunks = row_elems / 16;
+    const uint4* s4 = reinterpret_cast<const uint4*>(src) + t * chunks * kSrcVecs;
+    uint4* d4 = reinterpret_cast<uint4*>(dst) + static_cast<int64_t>(slot) * chunks;
+    for (int64_t c = threadIdx.x; c < chunks; c += kWriteThreads) {
+      const int kvh = static_cast<int>(c * 16 / a.head_dim);
+      const float sc = scales[static_cast<int64_t>(blk) * a.num_kv_heads + kvh];
+      float x[16];
+#pragma unroll
+      for (int v = 0; v < kSrcVecs; ++v) unpack16<SF>(s4[c * kSrcVecs + v], x + v * (16 / kSrcVecs));
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float qv = rintf(x[e] / sc);  // IEEE division, round half to even
+        qv = fminf(fmaxf(qv, -127.f), 127.f);
+        const uint32_t byte = static_cast<uint32_t>(static_cast<int32_t>(qv)) & 0xFFu;
+        w[e / 4] |= byte << (8 * (e % 4));
+      }
+      d4[c] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int SF, int KF>
+hipError_t launch_write(const CacheWriteArgs& a, int num_tokens, hipStream_t s) {
+  hipLaunchKernelGGL((cache_write_kernel<SF, KF>), dim3(num_tokens, 2), dim3(kWriteThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block copies for copy-on-write: pairs travel by value in the kernel
+// arguments, so no host-to-device transfer is needed.
+constexpr int kPairsPerLaunch = 64;
+constexpr int kCopyThreads = 256;
+constexpr int64_t kCopyChunk = kCopyThreads * 16 * 4;  // bytes per workgroup
+
+struct CopyBlocksArgs {
+  uint8_t* key_cache;
+  uint8_t* value_cache;
+  float* k_scales;
+  float* v_scales;
+  int64_t block_bytes;
+  int scale_stride;
+  int n;
+  int32_t src[kPairsPerLaunch];
+  int32_t dst[kPairsPerLaunch];
+};
+
+__global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(CopyBlocksArgs a) {
+  const int p = blockIdx.x;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kCopyChunk;
+  const bool is_v = blockIdx.z != 0;
+  uint8_t* base = is_v ? a.value_cache : a.key_cache;
+  const uint4* s = reinterpret_cast<const uint4*>(base + a.src[p] * a.block_bytes + c0);
+  uint4* d = reinterpret_cast<uint4*>(base + a.dst[p] * a.block_bytes + c0);
+  int64_t nvec = (a.block_bytes - c0) / 16;
+  if (nvec > kCopyChunk / 16) nvec = kCopyChunk / 16;
+  for (int64_t i = threadIdx.x; i < nvec; i += kCopyThreads) d[i] = s[i];
+  float* sc = is_v ? a.v_scales : a.k_scales;
+  if (sc && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i < a.scale_stride; i += kCopyThreads)
+      sc[static_cast<int64_t>(a.dst[p]) * a.scale_stride + i] =
+          sc[static_cast<int64_t>(a.src[p]) * a.scale_stride + i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 4;
+
+__global__ void __launch_bounds__(kStreamThreads) stream_copy_kernel(uint4* __restrict__ dst,
+                                                                     const uint4* __restrict__ src,
+                                                                     int64_t nvec) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kStreamThreads;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kStreamThreads + threadIdx.x;
+  for (; i + (kStreamUnroll - 1) * stride < nvec; i += kStreamUnroll * stride) {
+    uint4 r[kStreamUnroll];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) r[u] = src[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kStreamUnroll; ++u) dst[i + u * stride] = r[u];
+  }
+  for (; i < nvec; i += stride) dst[i] = src[i];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_reshape_and_cache(const void* k, const void* v, void* key_cache, void* value_cache,
+                          const float* k_scales, const float* v_scales,
+                          const int32_t* slot_mapping, int num_tokens, int num_kv_heads,
+                          int head_dim, int block_size, int num_blocks, int src_dtype,
+                          int kv_dtype, void* stream) {
+  PKV_API_BEGIN
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "bad shape: tokens=%d kv_heads=%d head_dim=%d "
+                     "block_size=%d num_blocks=%d", num_tokens, num_kv_heads, head_dim,
+                     block_size, num_blocks);
+  if (num_tokens == 0) return PKV_OK;
+  if (num_tokens > 65535 * 1024) return pkv::fail(PKV_ERR_INVALID_ARG, "too many tokens");
+  if (!k || !v || !key_cache || !value_cache || !slot_mapping)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  if (head_dim % 16) return pkv::fail(PKV_ERR_UNSUPPORTED, "head_dim %d not a multiple of 16", head_dim);
+  CacheWriteArgs a;
+  a.k = static_cast<const uint8_t*>(k);
+  a.v = static_cast<const uint8_t*>(v);
+  a.key_cache = static_cast<uint8_t*>(key_cache);
+  a.value_cache = static_cast<uint8_t*>(value_cache);
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.slots = slot_mapping;
+  a.num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (kv_dtype == PKV_I8) {
+    if (!k_scales || !v_scales) return pkv::fail(PKV_ERR_INVALID_ARG, "int8 cache needs scales");
+    switch (src_dtype) {
+      case PKV_F32: err = launch_write<PKV_F32, PKV_I8>(a, num_tokens, s); break;
+      case PKV_F16: err = launch_write<PKV_F16, PKV_I8>(a, num_tokens, s); break;
+      case PKV_BF16: err = launch_write<PKV_BF16, PKV_I8>(a, num_tokens, s); break;
+      default: return pkv::fail(PKV_ERR_INVALID_ARG, "int8 cache takes F32/F16/BF16 rows");
+    }
+  } else {
+    if (src_dtype != kv_dtype)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "float cache format %d takes rows of the same "
+                       "format (got %d)", kv_dtype, src_dtype);
+    switch (kv_dtype) {
+      case PKV_F32: err = launch_write<PKV_F32, PKV_F32>(a, num_tokens, s); break;
+      case PKV_F16: err = launch_write<PKV_F16, PKV_F16>(a, num_tokens, s); break;
+      case PKV_BF16: err = launch_write<PKV_BF16, PKV_BF16>(a, num_tokens, s); break;
+      default: return pkv::fail(PKV_ERR_INVALID_ARG, "unknown cache format %d", kv_dtype);
+    }
+  }
+  if (err != hipSuccess) return pkv::fail(PKV_ERR_HIP, "cache write launch: %s", hipGetErrorString(err));
+  return PKV_OK;
+  PKV_API_END
+}
+
+int pkv_copy_blocks(void* key_cache, void* value_cache, float* k_scales, float* v_scales,
+                    const int32_t* pairs, int n_pairs, size_t block_bytes, int num_blocks,
+                    int scale_stride, void* stream) {
+  PKV_API_BEGIN
+  if (n_pairs < 0 || num_blocks <= 0 || block_bytes == 0 || block_bytes % 16)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "bad count or block_bytes (%zu, multiple of 16)", block_bytes);
+  if (n_pairs == 0) return PKV_OK;
+  if (!key_cache || !value_cache || !pairs) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  if ((k_scales != nullptr) != (v_scales != nullptr) || (k_scales && scale_stride <= 0))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "scales must be given together with scale_stride > 0");
+  std::vector<char> is_dst(num_blocks, 0), is_src(num_blocks, 0);
+  for (int i = 0; i < n_pairs; ++i) {
+    const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "pair %d (%d, %d) outside [0, %d)", i, s, d, num_blocks);
+    if (is_dst[d]) return pkv::fail(PKV_ERR_INVALID_ARG, "block %d is a destination twice", d);
+    is_dst[d] = 1;
+    is_src[s] = 1;
+  }
+  for (int i = 0; i < n_pairs; ++i)
+    if (is_src[pairs[2 * i + 1]])
+      return pkv::fail(PKV_ERR_INVALID_ARG, "block %d is both source and destination", pairs[2 * i + 1]);
+  const int64_t chunks = (static_cast<int64_t>(block_bytes) + kCopyChunk - 1) / kCopyChunk;
+  if (chunks > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "block_bytes too large");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int base = 0; base < n_pairs; base += kPairsPerLaunch) {
+    CopyBlocksArgs a;
+    a.key_cache = static_cast<uint8_t*>(key_cache);
+    a.value_cache = static_cast<uint8_t*>(value_cache);
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.block_bytes = static_cast<int64_t>(block_bytes);
+    a.scale_stride = scale_stride;
+    a.n = n_pairs - base < kPairsPerLaunch ? n_pairs - base : kPairsPerLaunch;
+    for (int i = 0; i < a.n; ++i) {
+      a.src[i] = pairs[2 * (base + i)];
+      a.dst[i] = pairs[2 * (base + i) + 1];
+    }
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.n, static_cast<unsigned>(chunks), 2),
+                       dim3(kCopyThreads), 0, st, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return pkv::fail(PKV_ERR_HIP, "copy launch: %s", hipGetErrorString(err));
+  }
+  return PKV_OK;
+  PKV_API_END
+}
+
+int pkv_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  PKV_API_BEGIN
+  if (bytes == 0) return PKV_OK;
+  if (!dst || !src || bytes % 16 || reinterpret_cast<uintptr_t>(dst) % 16 ||
+      reinterpret_cast<uintptr_t>(src) % 16)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL or misaligned pointer, or size not a multiple of 16");
+  const int64_t nvec = static_cast<int64_t>(bytes / 16);
+  int64_t blocks = (nvec + kStreamThreads * kStreamUnroll - 1) / (kStreamThreads * kStreamUnroll);
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
+                     0, static_cast<hipStream_t>(stream), static_cast<uint4*>(dst),
+                     static_cast<const uint4*>(src), nvec);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return pkv::fail(PKV_ERR_HIP, "copy launch: %s", hipGetErrorString(err));
+  return PKV_OK;
+  PKV_API_END
+}
+
+}  // extern "C"

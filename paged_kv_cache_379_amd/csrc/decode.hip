@@ -1,0 +1,167 @@
+// Host side of pkv_paged_attention_decode: argument checks, the partition
+// policy, the workspace contract and the two launches (decode, then the merge
+// of partitions when the context is split).
+#include <cmath>
+
+#include "decode_dispatch.h"
+#include "pkv_internal.h"
+
+namespace pkv_dev {
+
+template <int QF>
+hipError_t launch_reduce(int head_dim, const DecodeArgs& a, unsigned grid, hipStream_t s) {
+  if (head_dim == 64)
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<QF, 64>), dim3(grid), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<QF, 128>), dim3(grid), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv_dev
+
+namespace {
+
+constexpr int kDefaultPartitionTokens = 512;
+
+// Blocks per partition, or max_blocks when the context is not split.
+// Returns -1 for an invalid request.
+int partition_blocks(int max_blocks, int block_size, int partition_size) {
+  if (max_blocks <= 0 || block_size <= 0 || partition_size < 0) return -1;
+  int tokens = partition_size;
+  if (tokens == 0) tokens = kDefaultPartitionTokens;
+  if (tokens % block_size) return -1;
+  const int pb = tokens / block_size;
+  return pb >= max_blocks ? max_blocks : pb;
+}
+
+bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+               int max_blocks) {
+  return num_seqs >= 0 && num_heads > 0 && num_kv_heads > 0 && num_heads % num_kv_heads == 0 &&
+         head_dim > 0 && block_size > 0 && max_blocks > 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                              int block_size, int max_blocks_per_seq, int partition_size) {
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
+    return 0;
+  const int pb = partition_blocks(max_blocks_per_seq, block_size, partition_size);
+  if (pb <= 0 || pb >= max_blocks_per_seq) return 0;
+  return pb * block_size;
+}
+
+size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                 int block_size, int max_blocks_per_seq, int partition_size) {
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
+    return 0;
+  const int pb = partition_blocks(max_blocks_per_seq, block_size, partition_size);
+  if (pb <= 0 || pb >= max_blocks_per_seq) return 0;
+  const size_t parts = (max_blocks_per_seq + pb - 1) / pb;
+  return static_cast<size_t>(num_seqs) * num_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
+                               const void* value_cache, const float* k_scales,
+                               const float* v_scales, const int32_t* block_tables,
+                               const int32_t* context_lens, int num_seqs, int num_heads,
+                               int num_kv_heads, int head_dim, int block_size,
+                               int max_blocks_per_seq, int num_blocks, float scale, int q_dtype,
+                               int kv_dtype, int partition_size, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  PKV_API_BEGIN
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
+      num_blocks <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG,
+                     "bad shape: seqs=%d heads=%d kv_heads=%d head_dim=%d block_size=%d "
+                     "max_blocks=%d num_blocks=%d",
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks);
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  const bool float_pair = (kv_dtype == PKV_F32 && q_dtype == PKV_F32) ||
+                          (kv_dtype == PKV_F16 && q_dtype == PKV_F16) ||
+                          (kv_dtype == PKV_BF16 && q_dtype == PKV_BF16);
+  const bool int8_pair = kv_dtype == PKV_I8 && (q_dtype == PKV_F16 || q_dtype == PKV_BF16);
+  if (!float_pair && !int8_pair)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "unsupported format pair q=%d kv=%d", q_dtype, kv_dtype);
+  if (int8_pair && (!k_scales || !v_scales))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "int8 cache needs k_scales and v_scales");
+  if (block_size != pkv_dev::kBlockSize)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d (built for %d)", block_size,
+                     pkv_dev::kBlockSize);
+  if (head_dim != 64 && head_dim != 128)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", head_dim);
+  const int group = num_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d (1, 2, 4, 8, 16)", group);
+  if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  const int pb = partition_blocks(max_blocks_per_seq, block_size, partition_size);
+  if (pb <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d",
+                     partition_size, block_size);
+  const int parts = (max_blocks_per_seq + pb - 1) / pb;
+  const size_t need = pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                block_size, max_blocks_per_seq, partition_size);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return pkv::fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                     workspace_bytes, workspace ? "" : ", NULL");
+  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * parts;
+  if (items > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "grid too large");
+
+  pkv_dev::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.key_cache = static_cast<const uint8_t*>(key_cache);
+  a.value_cache = static_cast<const uint8_t*>(value_cache);
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  float* ws = static_cast<float*>(workspace);
+  const size_t slots = static_cast<size_t>(num_seqs) * num_heads * parts;
+  a.ws_ml = need ? ws : nullptr;
+  a.ws_acc = need ? ws + 2 * slots : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.part_blocks = pb;
+  a.num_parts = parts;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bool ok = false;
+  hipError_t err = hipSuccess;
+  const unsigned grid = static_cast<unsigned>(items);
+  switch (kv_dtype) {
+    case PKV_F32: err = pkv_dev::launch_decode_f32(q_dtype, head_dim, group, a, grid, s, ok); break;
+    case PKV_F16: err = pkv_dev::launch_decode_f16(q_dtype, head_dim, group, a, grid, s, ok); break;
+    case PKV_BF16: err = pkv_dev::launch_decode_bf16(q_dtype, head_dim, group, a, grid, s, ok); break;
+    case PKV_I8: err = pkv_dev::launch_decode_i8(q_dtype, head_dim, group, a, grid, s, ok); break;
+    default: break;
+  }
+  if (!ok) return pkv::fail(PKV_ERR_UNSUPPORTED, "no kernel for this combination");
+  if (err != hipSuccess)
+    return pkv::fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
+  if (parts > 1) {
+    const unsigned rgrid = static_cast<unsigned>(static_cast<int64_t>(num_seqs) * num_heads);
+    switch (q_dtype) {
+      case PKV_F32: err = pkv_dev::launch_reduce<PKV_F32>(head_dim, a, rgrid, s); break;
+      case PKV_F16: err = pkv_dev::launch_reduce<PKV_F16>(head_dim, a, rgrid, s); break;
+      default: err = pkv_dev::launch_reduce<PKV_BF16>(head_dim, a, rgrid, s); break;
+    }
+    if (err != hipSuccess)
+      return pkv::fail(PKV_ERR_HIP, "partition merge launch: %s", hipGetErrorString(err));
+  }
+  return PKV_OK;
+  PKV_API_END
+}
+
+}  // extern "C"

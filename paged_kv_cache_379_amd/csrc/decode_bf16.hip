@@ -1,0 +1,13 @@
+// Decode kernels for BF16-format caches (queries in BF16).
+#include "decode_dispatch.h"
+
+namespace pkv_dev {
+
+hipError_t launch_decode_bf16(int q_dtype, int head_dim, int group, const DecodeArgs& a,
+                             unsigned grid, hipStream_t s, bool& ok) {
+  if (q_dtype == PKV_BF16) return launch_decode_dims<PKV_BF16, PKV_BF16>(head_dim, group, a, grid, s, ok);
+  ok = false;
+  return hipSuccess;
+}
+
+}  // namespace pkv_dev

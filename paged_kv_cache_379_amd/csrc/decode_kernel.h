@@ -1,0 +1,472 @@
+// Paged-attention decode kernels for gfx950 (CDNA4), templated on the cache
+// format, the query format, head_dim and the query-head group size.
+//
+// Page keys:
+//   [P1] "大模型KV Cache内存优化与PagedAttention显存管理机制详解" (yunthe.com)
+//   [P2] "大模型部署中KV Cache优化策略与显存管理实践教程" (yunthe.com)
+//   [P3] "vLLM推理框架源码初探：PagedAttention的显存管理设计" (trdm.cn)
+//
+// What is computed ([P1] "PagedAttention注意力计算流程" and its kernel sketch):
+// for a sequence's query head, token i of the context lives in physical block
+// table[i / 16] at offset i % 16; its score is scale * dot(q, k_i); the output
+// is the softmax-weighted sum of the v_i.  [P3] section 三 notes that the
+// scattered rows are best walked block by block, reading each block's rows
+// contiguously; that is what the wave loop below does.
+//
+// How it maps onto CDNA4 (this is not the sketch's one-thread-per-token shape):
+//   * one workgroup of NW wave64s per (sequence, kv head, context partition);
+//     with grouped-query attention the G query heads that share a kv head are
+//     all handled by that workgroup, so each K/V row is read from HBM once;
+//   * the waves of a workgroup take the partition's blocks round-robin; a wave
+//     reads a block's K rows of its kv head with 16-byte loads, LPR lanes per
+//     row (a 256-byte fp16 row of head_dim 128 is 16 lanes), RPI rows per load
+//     instruction, IPB instructions per 16-token block, then the same for V;
+//   * each lane holds its E query elements (per head) in registers, the dot
+//     product is finished by a DPP butterfly across the LPR lanes of a row;
+//   * every row group of a wave (the lanes that share token rows) keeps its own
+//     running softmax state (max, sum, E accumulators per head), so a block
+//     needs no cross-row traffic at all; the row groups and waves are merged
+//     exactly once at the end (shuffles, then LDS);
+//   * exp is exp2 with log2(e) folded into the scale; masking is by select, so
+//     slots past the context may hold anything (NaN included);
+//   * a partition that does not hold the whole context writes (max, sum,
+//     unnormalised accumulator) to the workspace and a second kernel merges
+//     the partitions of each (sequence, head) with the same exact rule.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pkv.h"
+
+namespace pkv_dev {
+
+constexpr int kBlockSize = 16;
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const uint8_t* key_cache;
+  const uint8_t* value_cache;
+  const float* k_scales;
+  const float* v_scales;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_ml;   // [B*H][num_parts][2]: running max (log2 domain) and sum
+  float* ws_acc;  // [B*H][num_parts][D]: unnormalised accumulators
+  int num_seqs;
+  int num_heads;
+  int num_kv_heads;
+  int max_blocks;
+  int num_blocks;
+  int part_blocks;  // blocks per partition
+  int num_parts;    // partitions per sequence in the grid
+  float scale_log2; // scale * log2(e)
+};
+
+template <int F> struct Format;
+template <> struct Format<PKV_F32> { static constexpr int kBytes = 4; };
+template <> struct Format<PKV_F16> { static constexpr int kBytes = 2; };
+template <> struct Format<PKV_BF16> { static constexpr int kBytes = 2; };
+template <> struct Format<PKV_I8> { static constexpr int kBytes = 1; };
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// 16 bytes of storage -> 16 / kBytes floats (exact conversions).
+template <int F> __device__ __forceinline__ void unpack16(const uint4& r, float* x);
+
+template <> __device__ __forceinline__ void unpack16<PKV_F32>(const uint4& r, float* x) {
+  x[0] = __uint_as_float(r.x);
+  x[1] = __uint_as_float(r.y);
+  x[2] = __uint_as_float(r.z);
+  x[3] = __uint_as_float(r.w);
+}
+
+template <> __device__ __forceinline__ void unpack16<PKV_F16>(const uint4& r, float* x) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const half2_t h = __builtin_bit_cast(half2_t, w[i]);
+    x[2 * i] = static_cast<float>(h.x);
+    x[2 * i + 1] = static_cast<float>(h.y);
+  }
+}
+
+template <> __device__ __forceinline__ void unpack16<PKV_BF16>(const uint4& r, float* x) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+template <> __device__ __forceinline__ void unpack16<PKV_I8>(const uint4& r, float* x) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      x[4 * i + j] = static_cast<float>(static_cast<int32_t>(w[i] << (24 - 8 * j)) >> 24);
+  }
+}
+
+// Round-to-nearest-even stores of an fp32 result in the query format.
+template <int F> __device__ __forceinline__ void store_elem(void* base, int64_t idx, float v);
+template <> __device__ __forceinline__ void store_elem<PKV_F32>(void* base, int64_t idx, float v) {
+  static_cast<float*>(base)[idx] = v;
+}
+template <> __device__ __forceinline__ void store_elem<PKV_F16>(void* base, int64_t idx, float v) {
+  static_cast<_Float16*>(base)[idx] = static_cast<_Float16>(v);
+}
+template <> __device__ __forceinline__ void store_elem<PKV_BF16>(void* base, int64_t idx, float v) {
+  uint32_t u = __float_as_uint(v);
+  uint16_t b;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) {
+    b = 0x7FC0;  // NaN
+  } else {
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    b = static_cast<uint16_t>(u >> 16);
+  }
+  static_cast<uint16_t*>(base)[idx] = b;
+}
+
+// E query elements (E * kBytes is a multiple of 16) -> fp32.
+template <int QF, int E>
+__device__ __forceinline__ void load_q(const void* base, int64_t elem, float* x) {
+  constexpr int kPer = 16 / Format<QF>::kBytes;
+  static_assert(E % kPer == 0, "query fragment must be whole 16-byte vectors");
+  const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) +
+                                                  elem * Format<QF>::kBytes);
+#pragma unroll
+  for (int v = 0; v < E / kPer; ++v) unpack16<QF>(p[v], x + v * kPer);
+}
+
+// DPP row permutations (within 16-lane rows).
+constexpr int kDppQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppRowMirror = 0x140;     // lane i <- lane 15-i within 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W consecutive lanes (result in every lane).
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (W >= 2) v += dpp<kDppQuadSwap1>(v);
+  if constexpr (W >= 4) v += dpp<kDppQuadSwap2>(v);
+  if constexpr (W >= 8) v += dpp<kDppRowHalfMirror>(v);
+  if constexpr (W >= 16) v += dpp<kDppRowMirror>(v);
+  if constexpr (W >= 32) v += __shfl_xor(v, 16);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Reduction over lanes that differ only in bits >= log2(FROM) (row groups).
+template <int FROM>
+__device__ __forceinline__ float across_groups_max(float v) {
+#pragma unroll
+  for (int off = FROM; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+template <int FROM>
+__device__ __forceinline__ float across_groups_sum(float v) {
+#pragma unroll
+  for (int off = FROM; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int KF, int QF, int D, int G, int NW>
+struct DecodeTile {
+  static constexpr int kEB = Format<KF>::kBytes;
+  static constexpr int kRow = D * kEB;        // bytes of one (token, kv head) row
+  static constexpr int kLPR = kRow / 16;      // lanes per row
+  static constexpr int kRPI = 64 / kLPR;      // rows per load instruction
+  static constexpr int kIPB = kBlockSize / kRPI;  // load instructions per block
+  static constexpr int kE = 16 / kEB;         // elements per lane per load
+  static_assert(kRow % 16 == 0 && kLPR >= 1 && kLPR <= 64 && 64 % kLPR == 0, "row shape");
+  static_assert(kRPI <= kBlockSize && kBlockSize % kRPI == 0, "block shape");
+};
+
+// Per-lane running softmax state of one row group for G heads.
+template <int G, int E>
+struct SoftmaxState {
+  float m[G];
+  float l[G];
+  float acc[G][E];
+};
+
+// Score, mask and accumulate NBLK blocks whose loads are issued together.
+template <int KF, int QF, int D, int G, int NW, int NBLK>
+__device__ __forceinline__ void process_blocks(
+    SoftmaxState<G, DecodeTile<KF, QF, D, G, NW>::kE>& st,
+    const float (&qf)[G][DecodeTile<KF, QF, D, G, NW>::kE], const uint8_t* kbase,
+    const uint8_t* vbase, int64_t blk_stride, int64_t row_stride, const int (&phys)[NBLK],
+    const int (&valid)[NBLK], const float (&ksc)[NBLK], const float (&vsc)[NBLK], int rg,
+    float scale_log2) {
+  using T = DecodeTile<KF, QF, D, G, NW>;
+  constexpr int E = T::kE, IPB = T::kIPB, RPI = T::kRPI, LPR = T::kLPR;
+  uint4 kr[NBLK][IPB], vr[NBLK][IPB];
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    const uint8_t* kp = kbase + static_cast<int64_t>(phys[b]) * blk_stride;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i)
+      kr[b][i] = *reinterpret_cast<const uint4*>(kp + static_cast<int64_t>(i * RPI) * row_stride);
+  }
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    const uint8_t* vp = vbase + static_cast<int64_t>(phys[b]) * blk_stride;
+#pragma unroll
+    for (int i = 0; i < IPB; ++i)
+      vr[b][i] = *reinterpret_cast<const uint4*>(vp + static_cast<int64_t>(i * RPI) * row_stride);
+  }
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    float s[G][IPB];
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      float kx[E];
+      unpack16<KF>(kr[b][i], kx);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) d = fmaf(qf[g][e], kx[e], d);
+        s[g][i] = d;
+      }
+    }
+    const float sc = scale_log2 * ksc[b];
+    const bool partial = valid[b] < kBlockSize;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        float v = group_sum<LPR>(s[g][i]) * sc;
+        if (partial && i * RPI + rg >= valid[b]) v = -INFINITY;
+        s[g][i] = v;
+      }
+    }
+    float vx[IPB][E];
+#pragma unroll
+    for (int i = 0; i < IPB; ++i) {
+      unpack16<KF>(vr[b][i], vx[i]);
+      if (partial && i * RPI + rg >= valid[b]) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) vx[i][e] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float bm = s[g][0];
+#pragma unroll
+      for (int i = 1; i < IPB; ++i) bm = fmaxf(bm, s[g][i]);
+      const float mn = fmaxf(st.m[g], bm);
+      const float ms = (mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(st.m[g] - ms);
+      float psum = 0.f;
+      float p[IPB];
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        p[i] = fast_exp2(s[g][i] - ms);
+        psum += p[i];
+      }
+      st.l[g] = st.l[g] * alpha + psum;
+      st.m[g] = mn;
+#pragma unroll
+      for (int e = 0; e < E; ++e) st.acc[g][e] *= alpha;
+#pragma unroll
+      for (int i = 0; i < IPB; ++i) {
+        const float pv = p[i] * vsc[b];
+#pragma unroll
+        for (int e = 0; e < E; ++e) st.acc[g][e] = fmaf(pv, vx[i][e], st.acc[g][e]);
+      }
+    }
+  }
+}
+
+template <int KF, int QF, int D, int G, int NW>
+__global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
+  using T = DecodeTile<KF, QF, D, G, NW>;
+  constexpr int E = T::kE, LPR = T::kLPR;
+  constexpr int UNROLL = 2;
+
+  __shared__ float s_acc[NW][G][D];
+  __shared__ float s_m[NW][G];
+  __shared__ float s_l[NW][G];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = lane % LPR;
+  const int rg = lane / LPR;
+
+  const int item = blockIdx.x;
+  const int part = item % a.num_parts;
+  const int sk = item / a.num_parts;
+  const int kvh = sk % a.num_kv_heads;
+  const int seq = sk / a.num_kv_heads;
+
+  int ctx = a.context_lens[seq];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
+  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
+  const int pb0 = part * a.part_blocks;
+  if (pb0 >= nblk && part != 0) return;  // partition past the context
+  const int pb1 = min(pb0 + a.part_blocks, nblk);
+  const int nparts_seq = (nblk + a.part_blocks - 1) / a.part_blocks;
+  const bool direct = nparts_seq <= 1;
+
+  float qf[G][E];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int h = kvh * G + g;
+    load_q<QF, E>(a.q, (static_cast<int64_t>(seq) * a.num_heads + h) * D + sub * E, qf[g]);
+  }
+
+  SoftmaxState<G, E> st;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    st.m[g] = -INFINITY;
+    st.l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[g][e] = 0.f;
+  }
+
+  const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * T::kRow;
+  const int64_t blk_stride = row_stride * kBlockSize;
+  const int64_t lane_off = static_cast<int64_t>(kvh) * T::kRow + sub * 16 + rg * row_stride;
+  const uint8_t* kbase = a.key_cache + lane_off;
+  const uint8_t* vbase = a.value_cache + lane_off;
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
+
+  // Blocks of this wave: pb0 + wave + NW * k for k < nk.
+  const int span = pb1 - pb0 - wave;
+  const int nk = span > 0 ? (span + NW - 1) / NW : 0;
+  for (int k0 = 0; k0 < nk; k0 += 64) {
+    const int kk = k0 + lane;
+    int tb = -1;
+    float tks = 1.f, tvs = 1.f;
+    if (kk < nk) {
+      tb = trow[pb0 + wave + NW * kk];
+      if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
+      if constexpr (KF == PKV_I8) {
+        if (tb >= 0) {
+          tks = a.k_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];
+          tvs = a.v_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];
+        }
+      }
+    }
+    const int kend = min(64, nk - k0);
+    int k = 0;
+    for (; k + UNROLL <= kend; k += UNROLL) {
+      int phys[UNROLL], valid[UNROLL];
+      float ks[UNROLL], vs[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int p = __builtin_amdgcn_readlane(tb, k + u);
+        const int j = pb0 + wave + NW * (k0 + k + u);
+        phys[u] = p < 0 ? 0 : p;
+        valid[u] = p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize);
+        ks[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k + u));
+        vs[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k + u));
+      }
+      process_blocks<KF, QF, D, G, NW, UNROLL>(st, qf, kbase, vbase, blk_stride, row_stride, phys,
+                                               valid, ks, vs, rg, a.scale_log2);
+    }
+    for (; k < kend; ++k) {
+      const int p = __builtin_amdgcn_readlane(tb, k);
+      const int j = pb0 + wave + NW * (k0 + k);
+      int phys[1] = {p < 0 ? 0 : p};
+      int valid[1] = {p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize)};
+      float ks[1] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k))};
+      float vs[1] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k))};
+      process_blocks<KF, QF, D, G, NW, 1>(st, qf, kbase, vbase, blk_stride, row_stride, phys, valid,
+                                          ks, vs, rg, a.scale_log2);
+    }
+  }
+
+  // Merge the row groups of this wave (exact rescaling to a common max).
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float M = across_groups_max<LPR>(st.m[g]);
+    const float f = fast_exp2(st.m[g] - (M == -INFINITY ? 0.f : M));
+    st.l[g] = across_groups_sum<LPR>(st.l[g] * f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) st.acc[g][e] = across_groups_sum<LPR>(st.acc[g][e] * f);
+    st.m[g] = M;
+  }
+  if (rg == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s_acc[wave][g][sub * E + e] = st.acc[g][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      s_m[wave][g] = st.m[g];
+      s_l[wave][g] = st.l[g];
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves and write the result (or this partition's partial).
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int g = idx / D;
+    const int d = idx % D;
+    float M = s_m[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+    const float ms = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(s_m[w][g] - ms);
+      L = fmaf(f, s_l[w][g], L);
+      O = fmaf(f, s_acc[w][g][d], O);
+    }
+    const int h = kvh * G + g;
+    const int64_t sh = static_cast<int64_t>(seq) * a.num_heads + h;
+    if (direct) {
+      store_elem<QF>(a.out, sh * D + d, L > 0.f ? O / L : 0.f);
+    } else {
+      const int64_t slot = sh * a.num_parts + part;
+      a.ws_acc[slot * D + d] = O;
+      if (d == 0) {
+        a.ws_ml[slot * 2] = M;
+        a.ws_ml[slot * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// Merge the partitions of each (sequence, head): one workgroup of D threads.
+template <int QF, int D>
+__global__ void __launch_bounds__(D) paged_decode_reduce_kernel(DecodeArgs a) {
+  const int sh = blockIdx.x;  // seq * num_heads + head
+  const int seq = sh / a.num_heads;
+  int ctx = a.context_lens[seq];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
+  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
+  const int np = (nblk + a.part_blocks - 1) / a.part_blocks;
+  if (np <= 1) return;  // the decode kernel wrote this output directly
+  const int d = threadIdx.x;
+  const float* ml = a.ws_ml + static_cast<int64_t>(sh) * a.num_parts * 2;
+  const float* acc = a.ws_acc + static_cast<int64_t>(sh) * a.num_parts * D;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  const float ms = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f, O = 0.f;
+  for (int p = 0; p < np; ++p) {
+    const float f = fast_exp2(ml[2 * p] - ms);
+    L = fmaf(f, ml[2 * p + 1], L);
+    O = fmaf(f, acc[static_cast<int64_t>(p) * D + d], O);
+  }
+  store_elem<QF>(a.out, static_cast<int64_t>(sh) * D + d, L > 0.f ? O / L : 0.f);
+}
+
+}  // namespace pkv_dev

@@ -25,3 +25,13 @@ def gpu_lib():
     import paged_kv_cache_379_amd as pkv
     pkv.load()  # raises if libpkv.so is missing
     return pkv
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stderr before it touches the device (flushed), so a
+    run that ends abruptly still shows which case was running."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield
