@@ -52,7 +52,7 @@ _SIGS = {
     "pkv_decode_workspace_size": (_c_size, [_c_int] * 7),
     "pkv_paged_attention_decode": (_c_int, [_vp] * 8 + [_c_int] * 7 + [ctypes.c_float] + [_c_int] * 3
                                    + [_vp, _c_size, _vp]),
-    "pkv_reshape_and_cache": (_c_int, [_vp] * 7 + [_c_int] * 6 + [_vp]),
+    "pkv_reshape_and_cache": (_c_int, [_vp] * 7 + [_c_int] * 7 + [_vp]),
     "pkv_copy_blocks": (_c_int, [_vp] * 4 + [_i32p, _c_int, _c_size, _c_int, _c_int, _vp]),
     "pkv_stream_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
     "pkv_allocator_create": (_c_int, [_c_int, _c_int, ctypes.POINTER(_vp)]),
@@ -80,6 +80,7 @@ _SIGS = {
                                      ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
 }
 EXPORTED = tuple(_SIGS)
+SIGNATURES = _SIGS
 
 
 def load(path=None):

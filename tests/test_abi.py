@@ -30,6 +30,47 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert lib.pkv_abi_version() == 1
 
 
+def _header_params():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(pkv_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", text):
+        params = " ".join(m.group(2).split())
+        out[m.group(1)] = [] if params in ("", "void") else [p.strip() for p in params.split(",")]
+    return out
+
+
+def _kind_c(decl):
+    if "*" in decl:
+        return "ptr"
+    if decl.startswith("size_t"):
+        return "size"
+    if decl.startswith("float") or decl.startswith("double"):
+        return "float"
+    return "int"
+
+
+def _kind_ctypes(t):
+    if t in (ctypes.c_void_p, ctypes.c_char_p) or hasattr(t, "_type_") and isinstance(t._type_, type):
+        return "ptr"
+    if t is ctypes.c_size_t:
+        return "size"
+    if t in (ctypes.c_float, ctypes.c_double):
+        return "float"
+    return "int"
+
+
+def test_binding_signatures_match_header():
+    """Every ctypes prototype has the header's parameter count and kinds
+    (pointer / size_t / float / integer), so no argument shifts position."""
+    params = _header_params()
+    assert sorted(params) == sorted(pkv.SIGNATURES)
+    for name, (_, argtypes) in pkv.SIGNATURES.items():
+        want = [_kind_c(p) for p in params[name]]
+        got = [_kind_ctypes(t) for t in argtypes]
+        assert got == want, f"{name}: binding {got} != header {want}"
+
+
 def test_workspace_size_and_partition_policy():
     # 70B-shaped layer: 2048 tokens, MB = 128, default partitions of 512 tokens
     assert pkv.decode_partition_size(32, 64, 64, 128, 16, 128) == 512
@@ -90,6 +131,7 @@ def test_decode_zero_sequences_is_a_no_op():
 def test_cache_write_and_copy_reject_bad_arguments():
     lib = pkv.load()
     r = lib.pkv_reshape_and_cache
+    assert len(r.argtypes) == 15
     assert r(1, 1, 1, 1, None, None, 1, 4, 2, 64, 16, 8, pkv.F16, pkv.F32, None) == pkv.ERR_INVALID_ARG
     assert r(1, 1, 1, 1, None, None, 1, 4, 2, 64, 16, 8, pkv.F16, pkv.I8, None) == pkv.ERR_INVALID_ARG
     assert r(1, 1, 1, 1, None, None, None, 4, 2, 64, 16, 8, pkv.F16, pkv.F16, None) == pkv.ERR_INVALID_ARG
