@@ -33,7 +33,7 @@ Readings of points the pages leave open (each also listed in the design doc):
 * the int8 cache write rounds ``x / scale`` in fp32, half to even, and
   saturates to [-127, 127].
 
-Pins (tests/test_oracle_decode.py, tests/test_oracle_cache_write.py): identity
+Pins (tests/oracle_pins.py, run by tests/test_oracle_decode.py): identity
 tables against torch's CPU ``scaled_dot_product_attention`` in fp64; pure-Python
 brute force on tiny shuffled tables; closed forms (ctx = 1, constant V, equal
 keys, scale 0); a one-hot score probe; permutation of physical block ids;
