@@ -131,6 +131,14 @@ template <> __device__ __forceinline__ void store_elem<PKV_BF16>(void* base, int
   static_cast<uint16_t*>(base)[idx] = b;
 }
 
+// 16-byte load of cache data that is read once: the non-temporal hint keeps
+// the stream from displacing reusable lines in the caches.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // E query elements (E * kBytes is a multiple of 16) -> fp32.
 template <int QF, int E>
 __device__ __forceinline__ void load_q(const void* base, int64_t elem, float* x) {
@@ -217,14 +225,14 @@ __device__ __forceinline__ void process_blocks(
     const uint8_t* kp = kbase + static_cast<int64_t>(phys[b]) * blk_stride;
 #pragma unroll
     for (int i = 0; i < IPB; ++i)
-      kr[b][i] = *reinterpret_cast<const uint4*>(kp + static_cast<int64_t>(i * RPI) * row_stride);
+      kr[b][i] = load_stream16(kp + static_cast<int64_t>(i * RPI) * row_stride);
   }
 #pragma unroll
   for (int b = 0; b < NBLK; ++b) {
     const uint8_t* vp = vbase + static_cast<int64_t>(phys[b]) * blk_stride;
 #pragma unroll
     for (int i = 0; i < IPB; ++i)
-      vr[b][i] = *reinterpret_cast<const uint4*>(vp + static_cast<int64_t>(i * RPI) * row_stride);
+      vr[b][i] = load_stream16(vp + static_cast<int64_t>(i * RPI) * row_stride);
   }
 #pragma unroll
   for (int b = 0; b < NBLK; ++b) {
