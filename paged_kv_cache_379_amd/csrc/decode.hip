@@ -111,6 +111,10 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   if (need > 0 && (!workspace || workspace_bytes < need))
     return pkv::fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
                      workspace_bytes, workspace ? "" : ", NULL");
+  // The kernels address one block's rows of a kv head with 32-bit offsets.
+  if (static_cast<int64_t>(num_kv_heads) * head_dim * pkv::elem_bytes(kv_dtype) * block_size >
+      INT32_MAX)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "a cache block is larger than 2 GiB");
   const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * parts;
   if (items > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "grid too large");
 

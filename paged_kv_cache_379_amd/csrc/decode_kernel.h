@@ -313,9 +313,15 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   const int sub = lane % LPR;
   const int rg = lane / LPR;
 
+  // Partition-major order: workgroup i runs on XCD i % 8, so consecutive ids
+  // must carry comparable work.  With the (sequence, kv head) pair fastest,
+  // each XCD sees every partition index and the same kv heads of every
+  // sequence (shared prefix blocks of a kv head then meet in one L2), and
+  // partitions past short contexts sit at the tail of the grid.
   const int item = blockIdx.x;
-  const int part = item % a.num_parts;
-  const int sk = item / a.num_parts;
+  const int nsk = a.num_seqs * a.num_kv_heads;
+  const int part = item / nsk;
+  const int sk = item - part * nsk;
   const int kvh = sk % a.num_kv_heads;
   const int seq = sk / a.num_kv_heads;
 
