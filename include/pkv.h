@@ -69,7 +69,10 @@ int pkv_abi_version(void);
  * Tokens per context partition that pkv_paged_attention_decode will use for
  * these shapes when called with the same `partition_size` (0 = automatic).
  * The result is a multiple of block_size, or 0 if the context is not split.
- * Returns 0 for invalid shapes.
+ * Returns 0 for invalid shapes.  The automatic choice depends on shapes only
+ * (never on device data): a table of up to 160 blocks is not split, a longer
+ * one is split into 64-block partitions, and the partitions are made smaller
+ * until num_seqs * num_kv_heads * partitions >= 512.
  */
 int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
                               int head_dim, int block_size,

@@ -23,7 +23,10 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-paramet
           f"-I{INCLUDE}", f"-I{CSRC}"]
 # Device code: gfx950 only; packed fp32 instructions off (the host pass warns
 # that it does not know the feature; that warning is harmless).
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # keep MFMA accumulators in ordinary VGPRs (no copies to and from AGPRs
+          # around the vector code that rescales them)
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 SOURCES = [
     "errors.cpp",

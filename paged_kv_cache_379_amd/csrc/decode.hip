@@ -21,17 +21,34 @@ hipError_t launch_reduce(int head_dim, const DecodeArgs& a, unsigned grid, hipSt
 
 namespace {
 
-constexpr int kDefaultPartitionTokens = 512;
+// Automatic partitioning (measured on MI355X with the five standard
+// workloads): a context of up to kWholeBlocks blocks is handled by one
+// workgroup per (sequence, kv head); longer ones are split into partitions of
+// kSplitBlocks blocks, so a few long sequences among short ones do not leave a
+// tail of long-running workgroups.  Independently, the grid is split further
+// until it has at least kMinItems workgroups (two per CU), so small batches
+// still fill the chip.
+constexpr int kWholeBlocks = 160;  // 2560 tokens at block size 16
+constexpr int kSplitBlocks = 64;   // 1024 tokens
+constexpr int64_t kMinItems = 512;
 
-// Blocks per partition, or max_blocks when the context is not split.
-// Returns -1 for an invalid request.
-int partition_blocks(int max_blocks, int block_size, int partition_size) {
+// Blocks per partition (max_blocks when the context is not split), or -1 for
+// an invalid request.  partition_size = 0 picks automatically.
+int partition_blocks(int num_seqs, int num_kv_heads, int max_blocks, int block_size,
+                     int partition_size) {
   if (max_blocks <= 0 || block_size <= 0 || partition_size < 0) return -1;
-  int tokens = partition_size;
-  if (tokens == 0) tokens = kDefaultPartitionTokens;
-  if (tokens % block_size) return -1;
-  const int pb = tokens / block_size;
-  return pb >= max_blocks ? max_blocks : pb;
+  if (partition_size > 0) {
+    if (partition_size % block_size) return -1;
+    const int pb = partition_size / block_size;
+    return pb >= max_blocks ? max_blocks : pb;
+  }
+  int pb = max_blocks > kWholeBlocks ? kSplitBlocks : max_blocks;
+  const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  if (pairs > 0 && pairs * ((max_blocks + pb - 1) / pb) < kMinItems) {
+    const int64_t parts = (kMinItems + pairs - 1) / pairs;
+    pb = static_cast<int>((max_blocks + parts - 1) / parts);
+  }
+  return pb < 1 ? 1 : (pb > max_blocks ? max_blocks : pb);
 }
 
 bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
@@ -48,7 +65,7 @@ int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int
                               int block_size, int max_blocks_per_seq, int partition_size) {
   if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
     return 0;
-  const int pb = partition_blocks(max_blocks_per_seq, block_size, partition_size);
+  const int pb = partition_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size);
   if (pb <= 0 || pb >= max_blocks_per_seq) return 0;
   return pb * block_size;
 }
@@ -57,7 +74,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, 
                                  int block_size, int max_blocks_per_seq, int partition_size) {
   if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
     return 0;
-  const int pb = partition_blocks(max_blocks_per_seq, block_size, partition_size);
+  const int pb = partition_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size);
   if (pb <= 0 || pb >= max_blocks_per_seq) return 0;
   const size_t parts = (max_blocks_per_seq + pb - 1) / pb;
   return static_cast<size_t>(num_seqs) * num_heads * parts * (head_dim + 2) * sizeof(float);
@@ -101,7 +118,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "scale is not finite");
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
     return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
-  const int pb = partition_blocks(max_blocks_per_seq, block_size, partition_size);
+  const int pb = partition_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size);
   if (pb <= 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d",
                      partition_size, block_size);

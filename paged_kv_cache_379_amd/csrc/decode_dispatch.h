@@ -33,8 +33,10 @@ hipError_t launch_decode_groups(int group, const DecodeArgs& a, unsigned grid, h
   } else {
     if (group == 1) {
       hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, 1, kDecodeWaves>), g, b, 0, s, a);
-    } else if (group >= 2 && group <= kMaxGroup) {
-      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves>), g, b, 0, s, a);
+    } else if (group >= 2 && group <= 8) {
+      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, true>), g, b, 0, s, a);
+    } else if (group > 8 && group <= kMaxGroup) {
+      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, false>), g, b, 0, s, a);
     } else {
       ok = false;
       return hipSuccess;

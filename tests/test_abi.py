@@ -72,13 +72,22 @@ def test_binding_signatures_match_header():
 
 
 def test_workspace_size_and_partition_policy():
-    # 70B-shaped layer: 2048 tokens, MB = 128, default partitions of 512 tokens
-    assert pkv.decode_partition_size(32, 64, 64, 128, 16, 128) == 512
-    assert pkv.decode_workspace_size(32, 64, 64, 128, 16, 128) == 32 * 64 * 4 * 130 * 4
-    # a partition as long as the table means no split and no workspace
+    # automatic policy: contexts up to 160 blocks stay whole ...
+    assert pkv.decode_partition_size(32, 64, 64, 128, 16, 128) == 0      # 70B-shaped, 2048 tokens
+    assert pkv.decode_workspace_size(32, 64, 64, 128, 16, 128) == 0
+    assert pkv.decode_partition_size(64, 64, 8, 128, 16, 157) == 0       # shared prefix, 2512 max
+    # ... longer tables split into 1024-token partitions
+    assert pkv.decode_partition_size(256, 32, 8, 128, 16, 256) == 1024   # int8 config, 4096 max
+    assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 256) == 256 * 32 * 4 * 130 * 4
+    # ... and small grids split further, to at least 512 workgroups
+    assert pkv.decode_partition_size(1, 8, 8, 128, 16, 2048) == 512      # 1 seq, 32k tokens
+    assert pkv.decode_partition_size(2, 4, 4, 64, 16, 7) == 16           # tiny: 7 partitions
+    assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7) == 2 * 4 * 7 * 66 * 4
+    # explicit sizes; one as long as the table means no split and no workspace
+    assert pkv.decode_partition_size(32, 64, 64, 128, 16, 128, 512) == 512
+    assert pkv.decode_workspace_size(32, 64, 64, 128, 16, 128, 512) == 32 * 64 * 4 * 130 * 4
     assert pkv.decode_partition_size(32, 64, 64, 128, 16, 128, 2048) == 0
     assert pkv.decode_workspace_size(32, 64, 64, 128, 16, 128, 4096) == 0
-    assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7) == 0          # 112 tokens < 512
     assert pkv.decode_partition_size(2, 4, 4, 64, 16, 7, 32) == 32
     assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7, 32) == 2 * 4 * 4 * 66 * 4
     # not a multiple of the block size -> invalid -> 0
