@@ -188,3 +188,64 @@ def test_shared_prefix_equals_duplicated(gpu_lib):
     wl.key_cache, wl.value_cache, wl.block_tables = kc, vc, tables
     dup = gpu_decode(gpu_lib, wl).cpu()
     assert torch.equal(shared, dup)
+
+
+@pytest.mark.parametrize("kv_fmt,q_fmt", [("f16", "f16"), ("bf16", "bf16"), ("i8", "f16")])
+@pytest.mark.parametrize("slope,pattern", [(0.02, "up"), (0.3, "up"), (5.0, "up"),
+                                           (0.3, "down"), (1.0, "saw")])
+def test_running_max_moves_along_the_context(gpu_lib, kv_fmt, q_fmt, slope, pattern):
+    """Scores that climb slowly (the grouped-query kernel's exponent base is
+    raised only now and then, weights grow up to 2^8 in between), climb fast
+    (raised at every block), fall, or saw-tooth; parity with the oracle."""
+    G, hkv, D = 8, 2, 128
+    lens = [700, 333, 64, 1000]
+    wl = W.make_workload(2, seed=31, num_seqs=len(lens), num_heads=G * hkv, num_kv_heads=hkv,
+                         head_dim=D, kv_fmt=kv_fmt, q_fmt=q_fmt, ctx=("fixed", lens),
+                         max_blocks=64)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal(wl.q.shape).astype(np.float32) * 0.1
+    q[:, :, 0] = 1.0
+    wl.q = W._round_to(q, q_fmt)
+    # dim 0 of each valid key follows the ramp; other dims stay N(0, 1)
+    for s, n in enumerate(lens):
+        pos = np.arange(n)
+        if pattern == "up":
+            ramp = slope * pos
+        elif pattern == "down":
+            ramp = slope * (n - pos)
+        else:
+            ramp = slope * (pos % 96)
+        ramp = ramp - ramp.max() + 40.0  # top score 40 / sqrt(D); a slope s moves the max by ~2s (log2) per block
+        blk, off = wl.block_tables[s, pos // 16], pos % 16
+        if kv_fmt == "i8":
+            codes = np.clip(np.rint(ramp[:, None] / wl.k_scales[blk]), -127, 127).astype(np.int8)
+            wl.key_cache[blk, off, :, 0] = codes
+        else:
+            vals = np.repeat(ramp[:, None], hkv, axis=1).astype(np.float32)
+            wl.key_cache[blk, off, :, 0] = W._round_to(vals, kv_fmt)
+    for part in (0, 256):
+        got = out_f64(gpu_decode(gpu_lib, wl, partition_size=part))
+        assert_parity(got, oracle_decode(wl), kv_fmt, q_fmt, with_output_rounding=True,
+                      label=f"{kv_fmt} slope {slope} {pattern} part={part}")
+
+
+@pytest.mark.parametrize("kv_fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("group", [4, 8, 16])
+def test_short_contexts_large_values(gpu_lib, kv_fmt, group):
+    """Two to nine tokens with V scaled by 4: a few large softmax weights, where
+    rounding the weights to 16 bits alone would show; parity with the oracle."""
+    hkv = 2
+    lens = [2, 3, 5, 9]
+    wl = W.make_workload(2, seed=17, num_seqs=len(lens), num_heads=group * hkv, num_kv_heads=hkv,
+                         head_dim=128, kv_fmt=kv_fmt, q_fmt=kv_fmt, ctx=("fixed", lens),
+                         max_blocks=4, poison_unused=True)
+    used = W.used_slot_mask(wl)
+    v32 = np.zeros(wl.value_cache.shape, np.float32)
+    rng = np.random.default_rng(3)
+    v32[used] = rng.standard_normal(v32[used].shape).astype(np.float32) * 4.0
+    wl.value_cache = np.where(used[:, :, None, None], W._round_to(v32, kv_fmt), wl.value_cache)
+    q32 = rng.standard_normal(wl.q.shape).astype(np.float32) * 2.0
+    wl.q = W._round_to(q32, kv_fmt)
+    got = out_f64(gpu_decode(gpu_lib, wl))
+    assert_parity(got, oracle_decode(wl), kv_fmt, kv_fmt, with_output_rounding=True,
+                  label=f"{kv_fmt} G={group} short contexts")
