@@ -34,9 +34,11 @@ hipError_t launch_decode_groups(int group, const DecodeArgs& a, unsigned grid, h
     if (group == 1) {
       hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, 1, kDecodeWaves>), g, b, 0, s, a);
     } else if (group >= 2 && group <= 8) {
-      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, true>), g, b, 0, s, a);
+      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, true>),
+                         g, b, 0, s, a);
     } else if (group > 8 && group <= kMaxGroup) {
-      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, false>), g, b, 0, s, a);
+      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, false>),
+                         g, b, 0, s, a);
     } else {
       ok = false;
       return hipSuccess;

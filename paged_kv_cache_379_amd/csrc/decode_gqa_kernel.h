@@ -222,6 +222,24 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
     }
   }
 
+  // V^T operands, read first so that their latency hides behind the scores
+  // and the softmax: lane (t, g) reads V elements (row 4g + j, dim 16c + t),
+  // j < 4, straight into the low and high halves of two registers.
+  u32x2_t vt[T::kTiles];
+  {
+    const uint8_t* vcol = tile + T::kTile + 4 * g * T::kPitch + 2 * t;
+#pragma unroll
+    for (int c = 0; c < T::kTiles; ++c) {
+      const uint8_t* p = vcol + 32 * c;
+      half2_t lo, hi;
+      lo.x = *reinterpret_cast<const _Float16*>(p);
+      lo.y = *reinterpret_cast<const _Float16*>(p + T::kPitch);
+      hi.x = *reinterpret_cast<const _Float16*>(p + 2 * T::kPitch);
+      hi.y = *reinterpret_cast<const _Float16*>(p + 3 * T::kPitch);
+      vt[c] = u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    }
+  }
+
   // S = K_blk . Q^T: lane (t, g) reads row t, dims 32c + 8g .. + 7.
   const uint8_t* krow = tile + t * T::kPitch + 16 * g;
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
@@ -282,16 +300,10 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
                    M::pack(w[2] - M::lo_value(h23), w[3] - M::hi_value(h23))};
   }
 
-  // O^T += V^T . P^T: lane (t, g) reads V elements (row 4g + j, dim 16c + t).
-  const uint8_t* vcol = tile + T::kTile + 4 * g * T::kPitch + 2 * t;
+  // O^T += V^T . P^T with the V^T operands read above.
 #pragma unroll
   for (int c = 0; c < T::kTiles; ++c) {
-    const uint8_t* p = vcol + 32 * c;
-    const uint32_t e0 = *reinterpret_cast<const uint16_t*>(p);
-    const uint32_t e1 = *reinterpret_cast<const uint16_t*>(p + T::kPitch);
-    const uint32_t e2 = *reinterpret_cast<const uint16_t*>(p + 2 * T::kPitch);
-    const uint32_t e3 = *reinterpret_cast<const uint16_t*>(p + 3 * T::kPitch);
-    const u32x2_t va = {e0 | (e1 << 16), e2 | (e3 << 16)};
+    const u32x2_t va = vt[c];
     st.acc[c] = M::k16(va, p_hi, st.acc[c]);
     if constexpr (!SPLIT) st.acc[c] = M::k16(va, p_lo, st.acc[c]);
   }
@@ -304,11 +316,12 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
   // Per-wave K/V tiles during the loop; the same bytes then hold the waves'
   // accumulators for the final merge.
   constexpr int kStageBytes = NW * 2 * T::kTile;
-  constexpr int kMergeBytes = NW * 16 * D * 4;
+  constexpr int kAccRow = D + 4;  // padded: the 16 columns' rows start in different banks
+  constexpr int kMergeBytes = NW * 16 * kAccRow * 4;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes];
   __shared__ float s_m[NW][16];
   __shared__ float s_l[NW][16];
-  float (*s_acc)[16][D] = reinterpret_cast<float (*)[16][D]>(smem);
+  float (*s_acc)[16][kAccRow] = reinterpret_cast<float (*)[16][kAccRow]>(smem);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -328,14 +341,18 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
   const int seq = sk / a.num_kv_heads;
   const int G = a.num_heads / a.num_kv_heads;
 
-  int ctx = a.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
-  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
   const int pb0 = part * a.part_blocks;
-  if (pb0 >= nblk && part != 0) return;  // partition past the context
-  const int pb1 = min(pb0 + a.part_blocks, nblk);
-  const int nparts_seq = (nblk + a.part_blocks - 1) / a.part_blocks;
-  const bool direct = nparts_seq <= 1;
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
+  // Issued together, before the context length is known, so that the
+  // prologue waits for one memory round trip instead of three: this wave's
+  // first table entries of the partition (as many as a full table holds;
+  // entries past the context are never used), the query, and the length.
+  int tb_first = -1;
+  {
+    const int span_full = min(pb0 + a.part_blocks, a.max_blocks) - pb0 - wave;
+    const int nk_full = span_full > 0 ? (span_full + NW - 1) / NW : 0;
+    if (lane < min(64, nk_full)) tb_first = trow[pb0 + wave + NW * lane];
+  }
 
   // Q^T operand: head t of this kv head's group (head t % 8 when SPLIT, so
   // columns t and t + 8 compute the same scores), dims 32c + 8g .. + 7.
@@ -351,6 +368,14 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
       qop[c] = hv ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+
+  int ctx = a.context_lens[seq];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
+  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
+  if (pb0 >= nblk && part != 0) return;  // partition past the context
+  const int pb1 = min(pb0 + a.part_blocks, nblk);
+  const int nparts_seq = (nblk + a.part_blocks - 1) / a.part_blocks;
+  const bool direct = nparts_seq <= 1;
 
   GqaState<KF, QF, D> st;
   st.m = -INFINITY;
@@ -375,7 +400,6 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
     goff[c] = static_cast<uint32_t>(r * row_stride + 16 * ch);
     soff[c] = static_cast<uint32_t>(r * T::kPitch + 16 * ch * (2 / T::kEB));
   }
-  const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
 
   // Blocks of this wave: pb0 + wave + NW * k for k < nk.  The loads of block
   // k + 1 are in flight while block k is computed from the LDS tiles.
@@ -386,7 +410,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
     int tb = -1;
     float tks = 1.f, tvs = 1.f;
     if (kk < nk) {
-      tb = trow[pb0 + wave + NW * kk];
+      tb = k0 == 0 ? tb_first : trow[pb0 + wave + NW * kk];
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
       if constexpr (KF == PKV_I8) {
         if (tb >= 0) {
@@ -402,17 +426,22 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
       const int p = __builtin_amdgcn_readlane(tb, k);
       return p < 0 ? 0 : p;
     };
-    GqaStage<KF, QF, D> stage;
-    gqa_load(stage, kbase, vbase, blk_stride, phys_of(0), goff);
-    for (int k = 0; k < kend; ++k) {
-      gqa_stage(tile, stage, soff);
-      if (k + 1 < kend) gqa_load(stage, kbase, vbase, blk_stride, phys_of(k + 1), goff);
+    // Block k of this chunk, already staged in LDS: scores, softmax, weighted sum.
+    auto compute = [&](int k) {
       const int p = __builtin_amdgcn_readlane(tb, k);
       const int j = pb0 + wave + NW * (k0 + k);
       const int valid = p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize);
       const float ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k));
       const float vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k));
       gqa_compute<KF, QF, D, SPLIT>(st, tile, qop, valid, ks, vs, t, g, a.scale_log2);
+    };
+    // The loads of block k + 1 are in flight while block k is computed.
+    GqaStage<KF, QF, D> r0;
+    gqa_load(r0, kbase, vbase, blk_stride, phys_of(0), goff);
+    for (int k = 0; k < kend; ++k) {
+      gqa_stage(tile, r0, soff);
+      if (k + 1 < kend) gqa_load(r0, kbase, vbase, blk_stride, phys_of(k + 1), goff);
+      compute(k);
     }
   }
   __syncthreads();  // the staging tiles become the merge buffer

@@ -325,14 +325,18 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   const int kvh = sk % a.num_kv_heads;
   const int seq = sk / a.num_kv_heads;
 
-  int ctx = a.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
-  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
   const int pb0 = part * a.part_blocks;
-  if (pb0 >= nblk && part != 0) return;  // partition past the context
-  const int pb1 = min(pb0 + a.part_blocks, nblk);
-  const int nparts_seq = (nblk + a.part_blocks - 1) / a.part_blocks;
-  const bool direct = nparts_seq <= 1;
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
+  // Issued together, before the context length is known, so that the
+  // prologue waits for one memory round trip instead of three: this wave's
+  // first table entries of the partition (as many as a full table holds;
+  // entries past the context are never used), the query, and the length.
+  int tb_first = -1;
+  {
+    const int span_full = min(pb0 + a.part_blocks, a.max_blocks) - pb0 - wave;
+    const int nk_full = span_full > 0 ? (span_full + NW - 1) / NW : 0;
+    if (lane < min(64, nk_full)) tb_first = trow[pb0 + wave + NW * lane];
+  }
 
   float qf[G][E];
 #pragma unroll
@@ -340,6 +344,14 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     const int h = kvh * G + g;
     load_q<QF, E>(a.q, (static_cast<int64_t>(seq) * a.num_heads + h) * D + sub * E, qf[g]);
   }
+
+  int ctx = a.context_lens[seq];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
+  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
+  if (pb0 >= nblk && part != 0) return;  // partition past the context
+  const int pb1 = min(pb0 + a.part_blocks, nblk);
+  const int nparts_seq = (nblk + a.part_blocks - 1) / a.part_blocks;
+  const bool direct = nparts_seq <= 1;
 
   SoftmaxState<G, E> st;
 #pragma unroll
@@ -355,7 +367,6 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   const int64_t lane_off = static_cast<int64_t>(kvh) * T::kRow + sub * 16 + rg * row_stride;
   const uint8_t* kbase = a.key_cache + lane_off;
   const uint8_t* vbase = a.value_cache + lane_off;
-  const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
 
   // Blocks of this wave: pb0 + wave + NW * k for k < nk.
   const int span = pb1 - pb0 - wave;
@@ -365,7 +376,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     int tb = -1;
     float tks = 1.f, tvs = 1.f;
     if (kk < nk) {
-      tb = trow[pb0 + wave + NW * kk];
+      tb = k0 == 0 ? tb_first : trow[pb0 + wave + NW * kk];
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
       if constexpr (KF == PKV_I8) {
         if (tb >= 0) {
