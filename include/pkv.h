@@ -72,11 +72,14 @@ int pkv_abi_version(void);
  * Returns 0 for invalid shapes.  The automatic choice depends on shapes only
  * (never on device data): a table of up to 160 blocks is not split, a longer
  * one is split into 64-block partitions, and the partitions are made smaller
- * until num_seqs * num_kv_heads * partitions >= 512.
+ * until num_seqs * num_kv_heads * partitions >= 512.  With a sliding window
+ * the table length is replaced by the most blocks the window can touch,
+ * ceil((W - 1) / block_size) + 1, and partitions start at the window.
  */
 int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
                               int head_dim, int block_size,
-                              int max_blocks_per_seq, int partition_size);
+                              int max_blocks_per_seq, int partition_size,
+                              int sliding_window);
 
 /*
  * Workspace bytes the decode needs for these shapes (0 when the context is
@@ -85,7 +88,8 @@ int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
  */
 size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                  int head_dim, int block_size,
-                                 int max_blocks_per_seq, int partition_size);
+                                 int max_blocks_per_seq, int partition_size,
+                                 int sliding_window);
 
 /*
  * Paged-attention decode ([P1] "PagedAttention注意力计算流程" and its kernel
@@ -103,6 +107,11 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  * exactly.  n = 0 gives an all-zero output.  Table entries past
  * ceil(n / bs) and slots past n are never read.
  *
+ * With sliding_window = W > 0 only tokens max(0, n - W) .. n - 1 are attended
+ * ([P2] "Sliding Window Attention控制长序列显存": only the most recent W
+ * tokens' KV is kept); table entries of blocks before the window are never
+ * read (they may be -1 after pkv_seq_trim_window).
+ *
  *   out          device, [B][H][D] in q_dtype (written)
  *   q            device, [B][H][D] in q_dtype: F32, F16 or BF16
  *   key_cache    device, see layout above, kv_dtype
@@ -118,6 +127,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  *   partition_size  tokens per partition, a multiple of block_size, or 0 for
  *                the library's choice; a value >= the longest possible context
  *                disables splitting
+ *   sliding_window  0 (attend to the whole context) or W > 0 tokens
  *   workspace    device scratch of >= pkv_decode_workspace_size(...) bytes
  *                (may be NULL when that is 0); fully rewritten by each call,
  *                so calls that share a workspace must be stream-ordered
@@ -135,8 +145,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
                                int num_heads, int num_kv_heads, int head_dim,
                                int block_size, int max_blocks_per_seq,
                                int num_blocks, float scale, int q_dtype,
-                               int kv_dtype, int partition_size, void* workspace,
-                               size_t workspace_bytes, void* stream);
+                               int kv_dtype, int partition_size, int sliding_window,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Cache write                                                               */
@@ -250,9 +260,23 @@ int pkv_seq_fork(pkv_allocator* a, int32_t seq, int32_t* child);
  */
 int pkv_seq_append_tokens(pkv_allocator* a, int32_t seq, int n, int32_t* slots_out,
                           int32_t* cow_pairs_out, int cow_cap, int* n_cow);
+/*
+ * Sliding window ([P2] "Sliding Window Attention控制长序列显存": only the most
+ * recent W tokens' KV is kept, so a sequence's cache stays constant in size):
+ * drop this sequence's reference to every block that holds no token of its
+ * last `window` tokens (blocks before the one holding token
+ * max(0, tokens - window)).  Their table entries become -1 (exported as the
+ * pad value; a lookup of their tokens is INDEX).  *n_released receives the
+ * number of blocks released; `released` (host int32[cap], may be NULL) their
+ * ids, in logical order.  INVALID_ARG (state unchanged) if window <= 0 or cap
+ * is too small for a non-NULL `released`.
+ */
+int pkv_seq_trim_window(pkv_allocator* a, int32_t seq, int window, int32_t* released,
+                        int cap, int* n_released);
 /* Release all of the sequence's block references and forget it. */
 int pkv_seq_free(pkv_allocator* a, int32_t seq);
 int pkv_seq_num_tokens(const pkv_allocator* a, int32_t seq, int* out);
+/* The sequence's logical block table (-1 for blocks released by a trim). */
 int pkv_seq_block_ids(const pkv_allocator* a, int32_t seq, int32_t* out, int cap, int* n);
 /* Physical block of a logical token ([P3] BlockTable lookup): INDEX if the
  * token's logical block has not been allocated. */
@@ -268,13 +292,14 @@ int pkv_export_block_tables(const pkv_allocator* a, const int32_t* seqs, int n,
 
 /*
  * Debug check of HOST copies of decode inputs: every table entry a context
- * reads lies in [0, num_blocks), and 0 <= len <= max_blocks * block_size.
+ * reads (only the window's blocks when sliding_window > 0) lies in
+ * [0, num_blocks), and 0 <= len <= max_blocks * block_size.
  * On INVALID_ARG, *bad_seq / *bad_block name the first offending entry
  * (bad_block = -1 for a bad length).
  */
 int pkv_validate_tables(const int32_t* tables, const int32_t* lens, int num_seqs,
                         int max_blocks, int block_size, int num_blocks,
-                        int* bad_seq, int* bad_block);
+                        int sliding_window, int* bad_seq, int* bad_block);
 
 #ifdef __cplusplus
 }  /* extern "C" */

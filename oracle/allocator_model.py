@@ -26,8 +26,10 @@ in extraction; the readings taken here:
   adds a reference; ``incref`` and ``fork`` (a child sequence that shares all
   of its parent's blocks) are that missing step;
 * ``usage_ratio = 1 - free / num_blocks``;
-* looking up a token whose logical block has not been allocated raises
-  IndexError.
+* looking up a token whose logical block has not been allocated (or has
+  been released behind a sliding window) raises IndexError;
+* ``seq_trim_window`` releases the blocks entirely before the last W tokens
+  ([P2] sliding window section); their table entries read -1.
 """
 
 
@@ -127,7 +129,7 @@ class AllocatorModel:
 
     def seq_fork(self, sid):
         parent = self.seqs[sid]
-        self.incref(parent["blocks"])
+        self.incref([b for b in parent["blocks"] if b >= 0])
         cid = self.next_seq
         self.next_seq += 1
         self.seqs[cid] = {"blocks": list(parent["blocks"]),
@@ -169,14 +171,32 @@ class AllocatorModel:
         seq["tokens"] = tokens
         return slots, cow
 
+    def seq_trim_window(self, sid, window):
+        """Release the blocks that hold no token of the last ``window`` tokens
+        ([P2] sliding window: tokens older than the window are dropped, so the
+        cache of a sequence stays within ceil(window / block_size) + 1 blocks).
+        Their table entries become -1; returns the released ids in order."""
+        if window <= 0:
+            raise ValueError("window must be positive")
+        seq = self.seqs[sid]
+        first_kept = max(0, seq["tokens"] - window) // self.block_size
+        released = []
+        for j in range(first_kept):
+            b = seq["blocks"][j]
+            if b >= 0:
+                released.append(b)
+                seq["blocks"][j] = -1
+        self.free(released)
+        return released
+
     def seq_free(self, sid):
         seq = self.seqs.pop(sid)
-        self.free(seq["blocks"])
+        self.free([b for b in seq["blocks"] if b >= 0])
 
     def seq_physical_block(self, sid, token):
         seq = self.seqs[sid]
         idx = token // self.block_size
-        if token < 0 or idx >= len(seq["blocks"]):
+        if token < 0 or idx >= len(seq["blocks"]) or seq["blocks"][idx] < 0:
             raise IndexError(f"token {token}: block {idx} not allocated")
         return seq["blocks"][idx]
 
@@ -186,6 +206,7 @@ class AllocatorModel:
             seq = self.seqs[sid]
             if len(seq["blocks"]) > max_blocks:
                 raise ValueError("max_blocks smaller than a sequence's table")
-            tables.append(seq["blocks"] + [pad] * (max_blocks - len(seq["blocks"])))
+            row = [b if b >= 0 else pad for b in seq["blocks"]]
+            tables.append(row + [pad] * (max_blocks - len(row)))
             lens.append(seq["tokens"])
         return tables, lens

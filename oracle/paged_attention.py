@@ -31,7 +31,9 @@ Readings of points the pages leave open (each also listed in the design doc):
 * table entries past ``ceil(ctx / bs)`` and cache slots past ``ctx`` are never
   read, whatever their contents;
 * the int8 cache write rounds ``x / scale`` in fp32, half to even, and
-  saturates to [-127, 127].
+  saturates to [-127, 127];
+* a sliding window W keeps the last W tokens, the decoded token included:
+  positions max(0, n - W) .. n - 1 ([P2] sliding window section).
 
 Pins (tests/oracle_pins.py, run by tests/test_oracle_decode.py): identity
 tables against torch's CPU ``scaled_dot_product_attention`` in fp64; pure-Python
@@ -68,15 +70,17 @@ def to_f64(x, fmt):
 
 
 def gather_context(key_cache, value_cache, table_row, n, block_size, kv_fmt,
-                   k_scales=None, v_scales=None):
-    """K and V of a sequence's first ``n`` logical tokens, as float64 [n, Hkv, D].
+                   k_scales=None, v_scales=None, start=0):
+    """K and V of a sequence's logical tokens start .. n - 1, as float64
+    [n - start, Hkv, D].
 
     Address translation of [P1] (kernel sketch) and [P3] section 二: token i is
     in logical block i // block_size at offset i % block_size, and the table row
-    gives the physical block of each logical block.
+    gives the physical block of each logical block.  Table entries of blocks
+    that hold no token of the range are not looked at.
     """
     num_blocks = key_cache.shape[0]
-    tokens = np.arange(n)
+    tokens = np.arange(start, n)
     logical_block = tokens // block_size
     offset = tokens % block_size
     if n and logical_block[-1] >= len(table_row):
@@ -95,18 +99,23 @@ def gather_context(key_cache, value_cache, table_row, n, block_size, kv_fmt,
 
 
 def paged_decode(q, q_fmt, key_cache, value_cache, kv_fmt, block_tables,
-                 context_lens, block_size, scale, k_scales=None, v_scales=None):
+                 context_lens, block_size, scale, k_scales=None, v_scales=None,
+                 window=0):
     """Decode attention over a paged KV cache; returns float64 [B, H, D].
 
     q            [B, H, D] in ``q_fmt``
     key_cache    [NB, block_size, Hkv, D] in ``kv_fmt``; value_cache likewise
     block_tables [B, MB] int, context_lens [B] int
     k_scales, v_scales [NB, Hkv] fp32 (``kv_fmt == "i8"`` only)
+    window       0, or the sliding window W: only the last W tokens of each
+                 context are attended to ([P2] "Sliding Window Attention控制
+                 长序列显存": only the most recent W tokens' KV is kept)
 
-    For each sequence s and query head h: gather the first ctx[s] keys and
-    values through the table, score each key as scale * dot(q, k), take the
-    softmax of the scores (shifted by their maximum, which leaves the softmax
-    unchanged and keeps exp in range) and return the weighted sum of values.
+    For each sequence s and query head h: gather the attended keys and values
+    through the table (the first ctx[s] tokens, or the last W of them), score
+    each key as scale * dot(q, k), take the softmax of the scores (shifted by
+    their maximum, which leaves the softmax unchanged and keeps exp in range)
+    and return the weighted sum of values.
     """
     q = np.asarray(q)
     num_seqs, num_heads, head_dim = q.shape
@@ -120,8 +129,9 @@ def paged_decode(q, q_fmt, key_cache, value_cache, kv_fmt, block_tables,
         n = int(context_lens[s])
         if n == 0:
             continue
+        start = max(0, n - int(window)) if window else 0
         k, v = gather_context(key_cache, value_cache, block_tables[s], n,
-                              block_size, kv_fmt, k_scales, v_scales)
+                              block_size, kv_fmt, k_scales, v_scales, start)
         qs = to_f64(q[s], q_fmt)
         for h in range(num_heads):
             kvh = h // group

@@ -48,9 +48,9 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 _SIGS = {
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_abi_version": (_c_int, []),
-    "pkv_decode_partition_size": (_c_int, [_c_int] * 7),
-    "pkv_decode_workspace_size": (_c_size, [_c_int] * 7),
-    "pkv_paged_attention_decode": (_c_int, [_vp] * 8 + [_c_int] * 7 + [ctypes.c_float] + [_c_int] * 3
+    "pkv_decode_partition_size": (_c_int, [_c_int] * 8),
+    "pkv_decode_workspace_size": (_c_size, [_c_int] * 8),
+    "pkv_paged_attention_decode": (_c_int, [_vp] * 8 + [_c_int] * 7 + [ctypes.c_float] + [_c_int] * 4
                                    + [_vp, _c_size, _vp]),
     "pkv_reshape_and_cache": (_c_int, [_vp] * 7 + [_c_int] * 7 + [_vp]),
     "pkv_copy_blocks": (_c_int, [_vp] * 4 + [_i32p, _c_int, _c_size, _c_int, _c_int, _vp]),
@@ -71,12 +71,13 @@ _SIGS = {
     "pkv_seq_fork": (_c_int, [_vp, ctypes.c_int32, _i32p]),
     "pkv_seq_append_tokens": (_c_int, [_vp, ctypes.c_int32, _c_int, _i32p, _i32p, _c_int,
                                        ctypes.POINTER(_c_int)]),
+    "pkv_seq_trim_window": (_c_int, [_vp, ctypes.c_int32, _c_int, _i32p, _c_int, ctypes.POINTER(_c_int)]),
     "pkv_seq_free": (_c_int, [_vp, ctypes.c_int32]),
     "pkv_seq_num_tokens": (_c_int, [_vp, ctypes.c_int32, ctypes.POINTER(_c_int)]),
     "pkv_seq_block_ids": (_c_int, [_vp, ctypes.c_int32, _i32p, _c_int, ctypes.POINTER(_c_int)]),
     "pkv_seq_physical_block": (_c_int, [_vp, ctypes.c_int32, _c_int, _i32p]),
     "pkv_export_block_tables": (_c_int, [_vp, _i32p, _c_int, _c_int, ctypes.c_int32, _i32p, _i32p]),
-    "pkv_validate_tables": (_c_int, [_i32p, _i32p, _c_int, _c_int, _c_int, _c_int,
+    "pkv_validate_tables": (_c_int, [_i32p, _i32p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
 }
 EXPORTED = tuple(_SIGS)
@@ -149,26 +150,28 @@ def _stream(stream):
 
 
 def decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                          max_blocks_per_seq, partition_size=0):
+                          max_blocks_per_seq, partition_size=0, window=0):
     return load().pkv_decode_partition_size(num_seqs, num_heads, num_kv_heads, head_dim,
-                                            block_size, max_blocks_per_seq, partition_size)
+                                            block_size, max_blocks_per_seq, partition_size,
+                                            window)
 
 
 def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                          max_blocks_per_seq, partition_size=0):
+                          max_blocks_per_seq, partition_size=0, window=0):
     return load().pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
-                                            block_size, max_blocks_per_seq, partition_size)
+                                            block_size, max_blocks_per_seq, partition_size,
+                                            window)
 
 
 def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context_lens,
                            block_size, scale, k_scales=None, v_scales=None,
-                           partition_size=0, workspace=None, stream=None):
+                           partition_size=0, workspace=None, stream=None, window=0):
     """Decode attention over a paged KV cache (see include/pkv.h).
 
     out, q [B, H, D]; key_cache, value_cache [NB, block_size, Hkv, D];
     block_tables int32 [B, MB]; context_lens int32 [B]; k/v_scales fp32
-    [NB, Hkv] for int8 caches.  A workspace of the needed size is allocated
-    from torch when none is given.
+    [NB, Hkv] for int8 caches; window: 0 or a sliding window in tokens.  A
+    workspace of the needed size is allocated from torch when none is given.
     """
     torch = _torch()
     lib = load()
@@ -181,7 +184,7 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [B, MB] and context_lens [B]")
     MB = block_tables.shape[1]
-    need = lib.pkv_decode_workspace_size(B, H, Hkv, D, bs, MB, partition_size)
+    need = lib.pkv_decode_workspace_size(B, H, Hkv, D, bs, MB, partition_size, window)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -192,7 +195,7 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
         _dev_ptr(block_tables, "block_tables", torch.int32),
         _dev_ptr(context_lens, "context_lens", torch.int32),
         B, H, Hkv, D, bs, MB, NB, float(scale), _fmt(q), _fmt(key_cache), int(partition_size),
-        _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream))
+        int(window), _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream))
     _check(rc)
     return out
 
@@ -236,14 +239,15 @@ def stream_copy(dst, src, nbytes=None, stream=None):
     _check(lib.pkv_stream_copy(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), nbytes, _stream(stream)))
 
 
-def validate_tables(tables, lens, block_size, num_blocks):
+def validate_tables(tables, lens, block_size, num_blocks, window=0):
     """Host check of decode tables; returns None or (bad_seq, bad_block)."""
     lib = load()
     t = np.ascontiguousarray(tables, dtype=np.int32)
     l = np.ascontiguousarray(lens, dtype=np.int32)
     bs_, bb = ctypes.c_int(), ctypes.c_int()
     rc = lib.pkv_validate_tables(t.ctypes.data_as(_i32p), l.ctypes.data_as(_i32p), t.shape[0],
-                                 t.shape[1], block_size, num_blocks, ctypes.byref(bs_), ctypes.byref(bb))
+                                 t.shape[1], block_size, num_blocks, window, ctypes.byref(bs_),
+                                 ctypes.byref(bb))
     if rc == OK:
         return None
     if rc == ERR_INVALID_ARG and bs_.value >= 0:
@@ -346,6 +350,15 @@ class BlockAllocator:
                                                cow.ctypes.data_as(_i32p), 1, ctypes.byref(ncow)))
         pairs = [(int(cow[0]), int(cow[1]))] if ncow.value else []
         return slots[:n].tolist(), pairs
+
+    def seq_trim_window(self, seq, window):
+        """Release the blocks behind the last ``window`` tokens; returns their ids."""
+        cap = len(self.seq_block_ids(seq))
+        out = np.empty(max(cap, 1), dtype=np.int32)
+        n = ctypes.c_int()
+        _check(self._lib.pkv_seq_trim_window(self._h, seq, window, out.ctypes.data_as(_i32p),
+                                             cap, ctypes.byref(n)))
+        return out[:n.value].tolist()
 
     def seq_free(self, seq):
         _check(self._lib.pkv_seq_free(self._h, seq))

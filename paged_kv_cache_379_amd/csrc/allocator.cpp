@@ -248,7 +248,8 @@ int pkv_seq_fork(pkv_allocator* a, int32_t seq, int32_t* child) {
   if (int rc = find_seq(a, seq, &parent)) return rc;
   if (a->next_seq == INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence ids exhausted");
   Sequence copy = *parent;
-  for (int32_t b : copy.blocks) ++a->refs[b];
+  for (int32_t b : copy.blocks)
+    if (b >= 0) ++a->refs[b];
   *child = a->next_seq++;
   a->seqs.emplace(*child, std::move(copy));
   return PKV_OK;
@@ -300,12 +301,43 @@ int pkv_seq_append_tokens(pkv_allocator* a, int32_t seq, int n, int32_t* slots_o
   PKV_API_END
 }
 
+int pkv_seq_trim_window(pkv_allocator* a, int32_t seq, int window, int32_t* released, int cap,
+                        int* n_released) {
+  PKV_API_BEGIN
+  if (int rc = check_alloc(a)) return rc;
+  if (window <= 0 || !n_released || (cap > 0 && !released))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "window must be positive and n_released given");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return pkv::fail(PKV_ERR_INVALID_ARG, "no sequence %d", seq);
+  Sequence& s = it->second;
+  // Blocks before the one holding token max(0, tokens - window) hold no token
+  // of the window.
+  const int64_t first_kept = std::max<int64_t>(0, s.tokens - window) / a->block_size;
+  int count = 0;
+  for (int64_t j = 0; j < first_kept; ++j) count += s.blocks[j] >= 0;
+  *n_released = count;
+  if (released && cap < count)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "capacity %d < %d released blocks", cap, count);
+  int k = 0;
+  for (int64_t j = 0; j < first_kept; ++j) {
+    const int32_t b = s.blocks[j];
+    if (b < 0) continue;
+    if (released) released[k] = b;
+    ++k;
+    a->drop_ref(b);
+    s.blocks[j] = -1;
+  }
+  return PKV_OK;
+  PKV_API_END
+}
+
 int pkv_seq_free(pkv_allocator* a, int32_t seq) {
   PKV_API_BEGIN
   if (int rc = check_alloc(a)) return rc;
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return pkv::fail(PKV_ERR_INVALID_ARG, "no sequence %d", seq);
-  for (int32_t b : it->second.blocks) a->drop_ref(b);
+  for (int32_t b : it->second.blocks)
+    if (b >= 0) a->drop_ref(b);
   a->seqs.erase(it);
   return PKV_OK;
   PKV_API_END
@@ -342,7 +374,7 @@ int pkv_seq_physical_block(const pkv_allocator* a, int32_t seq, int token, int32
   const Sequence* s;
   if (int rc = find_seq(a, seq, &s)) return rc;
   const int64_t idx = token / a->block_size;
-  if (token < 0 || idx >= static_cast<int64_t>(s->blocks.size()))
+  if (token < 0 || idx >= static_cast<int64_t>(s->blocks.size()) || s->blocks[idx] < 0)
     return pkv::fail(PKV_ERR_INDEX, "token %d: logical block %lld is not allocated", token,
                      static_cast<long long>(idx));
   *out = s->blocks[idx];
@@ -366,7 +398,7 @@ int pkv_export_block_tables(const pkv_allocator* a, const int32_t* seqs, int n, 
   for (int i = 0; i < n; ++i) {
     const Sequence& s = a->seqs.find(seqs[i])->second;
     int32_t* row = out_tables + static_cast<int64_t>(i) * max_blocks;
-    std::copy(s.blocks.begin(), s.blocks.end(), row);
+    for (size_t j = 0; j < s.blocks.size(); ++j) row[j] = s.blocks[j] >= 0 ? s.blocks[j] : pad;
     std::fill(row + s.blocks.size(), row + max_blocks, pad);
     out_lens[i] = static_cast<int32_t>(s.tokens);
   }
@@ -375,9 +407,10 @@ int pkv_export_block_tables(const pkv_allocator* a, const int32_t* seqs, int n, 
 }
 
 int pkv_validate_tables(const int32_t* tables, const int32_t* lens, int num_seqs, int max_blocks,
-                        int block_size, int num_blocks, int* bad_seq, int* bad_block) {
+                        int block_size, int num_blocks, int sliding_window, int* bad_seq,
+                        int* bad_block) {
   PKV_API_BEGIN
-  if (num_seqs < 0 || max_blocks < 0 || block_size <= 0 || num_blocks < 0 ||
+  if (num_seqs < 0 || max_blocks < 0 || block_size <= 0 || num_blocks < 0 || sliding_window < 0 ||
       (num_seqs > 0 && (!tables || !lens)))
     return pkv::fail(PKV_ERR_INVALID_ARG, "bad shape or NULL buffer");
   if (bad_seq) *bad_seq = -1;
@@ -390,7 +423,8 @@ int pkv_validate_tables(const int32_t* tables, const int32_t* lens, int num_seqs
                        static_cast<long long>(n), static_cast<long long>(max_blocks) * block_size);
     }
     const int64_t nb = (n + block_size - 1) / block_size;
-    for (int64_t j = 0; j < nb; ++j) {
+    const int64_t first = sliding_window > 0 ? std::max<int64_t>(0, n - sliding_window) : 0;
+    for (int64_t j = first / block_size; j < nb; ++j) {
       const int32_t b = tables[static_cast<int64_t>(s) * max_blocks + j];
       if (b < 0 || b >= num_blocks) {
         if (bad_seq) *bad_seq = s;

@@ -51,6 +51,14 @@ int partition_blocks(int num_seqs, int num_kv_heads, int max_blocks, int block_s
   return pb < 1 ? 1 : (pb > max_blocks ? max_blocks : pb);
 }
 
+// Table entries a context can read: all of them, or with a sliding window of
+// W tokens at most the blocks that W consecutive tokens can touch.
+int attended_blocks(int max_blocks, int block_size, int window) {
+  if (window <= 0) return max_blocks;
+  const int64_t span = (static_cast<int64_t>(window) - 1 + block_size - 1) / block_size + 1;
+  return span < max_blocks ? static_cast<int>(span) : max_blocks;
+}
+
 bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                int max_blocks) {
   return num_seqs >= 0 && num_heads > 0 && num_kv_heads > 0 && num_heads % num_kv_heads == 0 &&
@@ -62,21 +70,27 @@ bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int 
 extern "C" {
 
 int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                              int block_size, int max_blocks_per_seq, int partition_size) {
-  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
+                              int block_size, int max_blocks_per_seq, int partition_size,
+                              int sliding_window) {
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
+      sliding_window < 0)
     return 0;
-  const int pb = partition_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size);
-  if (pb <= 0 || pb >= max_blocks_per_seq) return 0;
+  const int eff = attended_blocks(max_blocks_per_seq, block_size, sliding_window);
+  const int pb = partition_blocks(num_seqs, num_kv_heads, eff, block_size, partition_size);
+  if (pb <= 0 || pb >= eff) return 0;
   return pb * block_size;
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                                 int block_size, int max_blocks_per_seq, int partition_size) {
-  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
+                                 int block_size, int max_blocks_per_seq, int partition_size,
+                                 int sliding_window) {
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
+      sliding_window < 0)
     return 0;
-  const int pb = partition_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size);
-  if (pb <= 0 || pb >= max_blocks_per_seq) return 0;
-  const size_t parts = (max_blocks_per_seq + pb - 1) / pb;
+  const int eff = attended_blocks(max_blocks_per_seq, block_size, sliding_window);
+  const int pb = partition_blocks(num_seqs, num_kv_heads, eff, block_size, partition_size);
+  if (pb <= 0 || pb >= eff) return 0;
+  const size_t parts = (eff + pb - 1) / pb;
   return static_cast<size_t>(num_seqs) * num_heads * parts * (head_dim + 2) * sizeof(float);
 }
 
@@ -86,8 +100,8 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
                                const int32_t* context_lens, int num_seqs, int num_heads,
                                int num_kv_heads, int head_dim, int block_size,
                                int max_blocks_per_seq, int num_blocks, float scale, int q_dtype,
-                               int kv_dtype, int partition_size, void* workspace,
-                               size_t workspace_bytes, void* stream) {
+                               int kv_dtype, int partition_size, int sliding_window,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   PKV_API_BEGIN
   if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
       num_blocks <= 0)
@@ -118,13 +132,17 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "scale is not finite");
   if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
     return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
-  const int pb = partition_blocks(num_seqs, num_kv_heads, max_blocks_per_seq, block_size, partition_size);
+  if (sliding_window < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "sliding_window %d is negative", sliding_window);
+  const int eff = attended_blocks(max_blocks_per_seq, block_size, sliding_window);
+  const int pb = partition_blocks(num_seqs, num_kv_heads, eff, block_size, partition_size);
   if (pb <= 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d",
                      partition_size, block_size);
-  const int parts = (max_blocks_per_seq + pb - 1) / pb;
-  const size_t need = pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                block_size, max_blocks_per_seq, partition_size);
+  const int parts = (eff + pb - 1) / pb;
+  const size_t need =
+      pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, partition_size, sliding_window);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return pkv::fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
                      workspace_bytes, workspace ? "" : ", NULL");
@@ -155,6 +173,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   a.num_blocks = num_blocks;
   a.part_blocks = pb;
   a.num_parts = parts;
+  a.window = sliding_window;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
 
   hipStream_t s = static_cast<hipStream_t>(stream);

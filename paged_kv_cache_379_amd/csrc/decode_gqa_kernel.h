@@ -207,14 +207,15 @@ struct GqaState {
 template <int KF, int QF, int D, bool SPLIT>
 __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* tile,
                                             const u32x4_t (&qop)[GqaTile<KF, QF, D>::kSlices],
-                                            int valid, float ksc, float vsc, int t, int g,
+                                            int lo, int valid, float ksc, float vsc, int t, int g,
                                             float scale_log2) {
   using T = GqaTile<KF, QF, D>;
   using M = Mfma<QF>;
-  // Rows past the context: zero their V elements (this lane's 16-byte chunks
-  // of row t) so the weighted sum never touches what those slots held.
-  if (valid < kBlockSize) {
-    if (t >= valid) {
+  // Rows outside the attended tokens lo <= offset < valid (lo > 0 only in the
+  // first block of a sliding window): zero their V elements (this lane's
+  // 16-byte chunks of row t) so the weighted sum never touches those slots.
+  if (valid < kBlockSize || lo > 0) {
+    if (t >= valid || t < lo) {
 #pragma unroll
       for (int c = 0; c < T::kSlices; ++c)
         *reinterpret_cast<u32x4_t*>(tile + T::kTile + t * T::kPitch + 64 * c + 16 * g) =
@@ -251,7 +252,7 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
   const float sc = scale_log2 * ksc;
   float sv[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sv[i] = (4 * g + i < valid) ? s[i] * sc : -INFINITY;
+  for (int i = 0; i < 4; ++i) sv[i] = (4 * g + i < valid && 4 * g + i >= lo) ? s[i] * sc : -INFINITY;
   float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   {
     const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
@@ -341,17 +342,20 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
   const int seq = sk / a.num_kv_heads;
   const int G = a.num_heads / a.num_kv_heads;
 
-  const int pb0 = part * a.part_blocks;
   const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
   // Issued together, before the context length is known, so that the
   // prologue waits for one memory round trip instead of three: this wave's
   // first table entries of the partition (as many as a full table holds;
   // entries past the context are never used), the query, and the length.
+  // With a sliding window the partitions start at the window, which depends
+  // on the length, so the table is read after it.
+  const bool early_table = a.window == 0;
   int tb_first = -1;
-  {
-    const int span_full = min(pb0 + a.part_blocks, a.max_blocks) - pb0 - wave;
+  if (early_table) {
+    const int pb0e = part * a.part_blocks;
+    const int span_full = min(pb0e + a.part_blocks, a.max_blocks) - pb0e - wave;
     const int nk_full = span_full > 0 ? (span_full + NW - 1) / NW : 0;
-    if (lane < min(64, nk_full)) tb_first = trow[pb0 + wave + NW * lane];
+    if (lane < min(64, nk_full)) tb_first = trow[pb0e + wave + NW * lane];
   }
 
   // Q^T operand: head t of this kv head's group (head t % 8 when SPLIT, so
@@ -369,12 +373,12 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
     }
   }
 
-  int ctx = a.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
-  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-  if (pb0 >= nblk && part != 0) return;  // partition past the context
-  const int pb1 = min(pb0 + a.part_blocks, nblk);
-  const int nparts_seq = (nblk + a.part_blocks - 1) / a.part_blocks;
+  const Span sp = attended_span(a, seq);
+  const int ctx = sp.ctx;
+  const int pb0 = sp.first_block + part * a.part_blocks;
+  if (pb0 >= sp.end_block && part != 0) return;  // partition past the context
+  const int pb1 = min(pb0 + a.part_blocks, sp.end_block);
+  const int nparts_seq = (sp.end_block - sp.first_block + a.part_blocks - 1) / a.part_blocks;
   const bool direct = nparts_seq <= 1;
 
   GqaState<KF, QF, D> st;
@@ -410,7 +414,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
     int tb = -1;
     float tks = 1.f, tvs = 1.f;
     if (kk < nk) {
-      tb = k0 == 0 ? tb_first : trow[pb0 + wave + NW * kk];
+      tb = (k0 == 0 && early_table) ? tb_first : trow[pb0 + wave + NW * kk];
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
       if constexpr (KF == PKV_I8) {
         if (tb >= 0) {
@@ -430,10 +434,11 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
     auto compute = [&](int k) {
       const int p = __builtin_amdgcn_readlane(tb, k);
       const int j = pb0 + wave + NW * (k0 + k);
+      const int lo = max(0, sp.first - j * kBlockSize);
       const int valid = p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize);
       const float ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k));
       const float vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k));
-      gqa_compute<KF, QF, D, SPLIT>(st, tile, qop, valid, ks, vs, t, g, a.scale_log2);
+      gqa_compute<KF, QF, D, SPLIT>(st, tile, qop, lo, valid, ks, vs, t, g, a.scale_log2);
     };
     // The loads of block k + 1 are in flight while block k is computed.
     GqaStage<KF, QF, D> r0;

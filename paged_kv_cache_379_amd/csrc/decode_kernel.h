@@ -61,8 +61,27 @@ struct DecodeArgs {
   int num_blocks;
   int part_blocks;  // blocks per partition
   int num_parts;    // partitions per sequence in the grid
+  int window;       // sliding window in tokens, 0 = the whole context
   float scale_log2; // scale * log2(e)
 };
+
+// The attended part of a sequence's context: its length clamped to the table,
+// the first attended token (the last `window` tokens when a sliding window is
+// set) and the logical blocks [first_block, end_block) that hold them.
+// Partition p covers blocks first_block + p * part_blocks onwards.
+struct Span {
+  int ctx;
+  int first;
+  int first_block;
+  int end_block;
+};
+
+__device__ __forceinline__ Span attended_span(const DecodeArgs& a, int seq) {
+  int ctx = a.context_lens[seq];
+  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
+  const int first = a.window > 0 ? max(0, ctx - a.window) : 0;
+  return Span{ctx, first, first / kBlockSize, (ctx + kBlockSize - 1) / kBlockSize};
+}
 
 template <int F> struct Format;
 template <> struct Format<PKV_F32> { static constexpr int kBytes = 4; };
@@ -215,8 +234,8 @@ __device__ __forceinline__ void process_blocks(
     SoftmaxState<G, DecodeTile<KF, QF, D, G, NW>::kE>& st,
     const float (&qf)[G][DecodeTile<KF, QF, D, G, NW>::kE], const uint8_t* kbase,
     const uint8_t* vbase, int64_t blk_stride, int64_t row_stride, const int (&phys)[NBLK],
-    const int (&valid)[NBLK], const float (&ksc)[NBLK], const float (&vsc)[NBLK], int rg,
-    float scale_log2) {
+    const int (&lo)[NBLK], const int (&valid)[NBLK], const float (&ksc)[NBLK],
+    const float (&vsc)[NBLK], int rg, float scale_log2) {
   using T = DecodeTile<KF, QF, D, G, NW>;
   constexpr int E = T::kE, IPB = T::kIPB, RPI = T::kRPI, LPR = T::kLPR;
   uint4 kr[NBLK][IPB], vr[NBLK][IPB];
@@ -250,13 +269,16 @@ __device__ __forceinline__ void process_blocks(
       }
     }
     const float sc = scale_log2 * ksc[b];
-    const bool partial = valid[b] < kBlockSize;
+    // tokens lo <= offset < valid of the block are attended (lo > 0 only in
+    // the first block of a sliding window)
+    const bool partial = valid[b] < kBlockSize || lo[b] > 0;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
       for (int i = 0; i < IPB; ++i) {
         float v = group_sum<LPR>(s[g][i]) * sc;
-        if (partial && i * RPI + rg >= valid[b]) v = -INFINITY;
+        const int off = i * RPI + rg;
+        if (partial && (off >= valid[b] || off < lo[b])) v = -INFINITY;
         s[g][i] = v;
       }
     }
@@ -264,7 +286,8 @@ __device__ __forceinline__ void process_blocks(
 #pragma unroll
     for (int i = 0; i < IPB; ++i) {
       unpack16<KF>(vr[b][i], vx[i]);
-      if (partial && i * RPI + rg >= valid[b]) {
+      const int off = i * RPI + rg;
+      if (partial && (off >= valid[b] || off < lo[b])) {
 #pragma unroll
         for (int e = 0; e < E; ++e) vx[i][e] = 0.f;
       }
@@ -325,17 +348,20 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   const int kvh = sk % a.num_kv_heads;
   const int seq = sk / a.num_kv_heads;
 
-  const int pb0 = part * a.part_blocks;
   const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
   // Issued together, before the context length is known, so that the
   // prologue waits for one memory round trip instead of three: this wave's
   // first table entries of the partition (as many as a full table holds;
   // entries past the context are never used), the query, and the length.
+  // With a sliding window the partitions start at the window, which depends
+  // on the length, so the table is read after it.
+  const bool early_table = a.window == 0;
   int tb_first = -1;
-  {
-    const int span_full = min(pb0 + a.part_blocks, a.max_blocks) - pb0 - wave;
+  if (early_table) {
+    const int pb0e = part * a.part_blocks;
+    const int span_full = min(pb0e + a.part_blocks, a.max_blocks) - pb0e - wave;
     const int nk_full = span_full > 0 ? (span_full + NW - 1) / NW : 0;
-    if (lane < min(64, nk_full)) tb_first = trow[pb0 + wave + NW * lane];
+    if (lane < min(64, nk_full)) tb_first = trow[pb0e + wave + NW * lane];
   }
 
   float qf[G][E];
@@ -345,12 +371,12 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     load_q<QF, E>(a.q, (static_cast<int64_t>(seq) * a.num_heads + h) * D + sub * E, qf[g]);
   }
 
-  int ctx = a.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
-  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-  if (pb0 >= nblk && part != 0) return;  // partition past the context
-  const int pb1 = min(pb0 + a.part_blocks, nblk);
-  const int nparts_seq = (nblk + a.part_blocks - 1) / a.part_blocks;
+  const Span sp = attended_span(a, seq);
+  const int ctx = sp.ctx;
+  const int pb0 = sp.first_block + part * a.part_blocks;
+  if (pb0 >= sp.end_block && part != 0) return;  // partition past the context
+  const int pb1 = min(pb0 + a.part_blocks, sp.end_block);
+  const int nparts_seq = (sp.end_block - sp.first_block + a.part_blocks - 1) / a.part_blocks;
   const bool direct = nparts_seq <= 1;
 
   SoftmaxState<G, E> st;
@@ -376,7 +402,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     int tb = -1;
     float tks = 1.f, tvs = 1.f;
     if (kk < nk) {
-      tb = k0 == 0 ? tb_first : trow[pb0 + wave + NW * kk];
+      tb = (k0 == 0 && early_table) ? tb_first : trow[pb0 + wave + NW * kk];
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
       if constexpr (KF == PKV_I8) {
         if (tb >= 0) {
@@ -388,29 +414,31 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     const int kend = min(64, nk - k0);
     int k = 0;
     for (; k + UNROLL <= kend; k += UNROLL) {
-      int phys[UNROLL], valid[UNROLL];
+      int phys[UNROLL], lo[UNROLL], valid[UNROLL];
       float ks[UNROLL], vs[UNROLL];
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int p = __builtin_amdgcn_readlane(tb, k + u);
         const int j = pb0 + wave + NW * (k0 + k + u);
         phys[u] = p < 0 ? 0 : p;
+        lo[u] = max(0, sp.first - j * kBlockSize);
         valid[u] = p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize);
         ks[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k + u));
         vs[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k + u));
       }
       process_blocks<KF, QF, D, G, NW, UNROLL>(st, qf, kbase, vbase, blk_stride, row_stride, phys,
-                                               valid, ks, vs, rg, a.scale_log2);
+                                               lo, valid, ks, vs, rg, a.scale_log2);
     }
     for (; k < kend; ++k) {
       const int p = __builtin_amdgcn_readlane(tb, k);
       const int j = pb0 + wave + NW * (k0 + k);
       int phys[1] = {p < 0 ? 0 : p};
+      int lo[1] = {max(0, sp.first - j * kBlockSize)};
       int valid[1] = {p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize)};
       float ks[1] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k))};
       float vs[1] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k))};
-      process_blocks<KF, QF, D, G, NW, 1>(st, qf, kbase, vbase, blk_stride, row_stride, phys, valid,
-                                          ks, vs, rg, a.scale_log2);
+      process_blocks<KF, QF, D, G, NW, 1>(st, qf, kbase, vbase, blk_stride, row_stride, phys, lo,
+                                          valid, ks, vs, rg, a.scale_log2);
     }
   }
 
@@ -474,10 +502,8 @@ template <int QF, int D>
 __global__ void __launch_bounds__(D) paged_decode_reduce_kernel(DecodeArgs a) {
   const int sh = blockIdx.x;  // seq * num_heads + head
   const int seq = sh / a.num_heads;
-  int ctx = a.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
-  const int nblk = (ctx + kBlockSize - 1) / kBlockSize;
-  const int np = (nblk + a.part_blocks - 1) / a.part_blocks;
+  const Span sp = attended_span(a, seq);
+  const int np = (sp.end_block - sp.first_block + a.part_blocks - 1) / a.part_blocks;
   if (np <= 1) return;  // the decode kernel wrote this output directly
   const int d = threadIdx.x;
   const float* ml = a.ws_ml + static_cast<int64_t>(sh) * a.num_parts * 2;

@@ -45,7 +45,8 @@ def upload(wl):
     return d
 
 
-def gpu_decode(pkv, wl, dev=None, partition_size=0, block_tables=None, context_lens=None):
+def gpu_decode(pkv, wl, dev=None, partition_size=0, block_tables=None, context_lens=None,
+               window=0):
     dev = dev or upload(wl)
     out = torch.empty_like(dev["q"])
     pkv.paged_attention_decode(
@@ -53,7 +54,7 @@ def gpu_decode(pkv, wl, dev=None, partition_size=0, block_tables=None, context_l
         dev["block_tables"] if block_tables is None else block_tables,
         dev["context_lens"] if context_lens is None else context_lens,
         wl.block_size, wl.scale, dev["k_scales"], dev["v_scales"],
-        partition_size=partition_size)
+        partition_size=partition_size, window=window)
     torch.cuda.synchronize()
     return out
 
@@ -62,7 +63,8 @@ def out_f64(out):
     return out.float().cpu().numpy().astype(np.float64)
 
 
-def oracle_decode(wl, seqs=None, context_lens=None, key_cache=None, value_cache=None):
+def oracle_decode(wl, seqs=None, context_lens=None, key_cache=None, value_cache=None,
+                  window=0):
     sel = slice(None) if seqs is None else np.asarray(seqs)
     lens = wl.context_lens if context_lens is None else context_lens
     return pa.paged_decode(
@@ -70,7 +72,7 @@ def oracle_decode(wl, seqs=None, context_lens=None, key_cache=None, value_cache=
         wl.key_cache if key_cache is None else key_cache,
         wl.value_cache if value_cache is None else value_cache,
         wl.kv_fmt, wl.block_tables[sel], np.asarray(lens)[sel], wl.block_size, wl.scale,
-        wl.k_scales, wl.v_scales)
+        wl.k_scales, wl.v_scales, window=window)
 
 
 def assert_parity(got, ref, kv_fmt, out_fmt=None, with_output_rounding=False, label=""):

@@ -298,9 +298,64 @@ def pin_cache_write_int8(pa):
     assert list(kw[0, 1, 0, :6]) == [2, -2, 4, 0, 127, -127]
 
 
+def pin_window_equals_contiguous_tail(pa):
+    """Sliding window W: paged decode == torch SDPA on the contiguous last W
+    tokens ([P2] sliding window: only the most recent W tokens take part),
+    for windows below, at and across block boundaries and past the context."""
+    rng = np.random.default_rng(23)
+    h, hkv, d = 4, 2, 32
+    lens = [37, 100, 16, 1, 64]
+    k_list = [rng.standard_normal((n, hkv, d)) for n in lens]
+    v_list = [rng.standard_normal((n, hkv, d)) for n in lens]
+    q = rng.standard_normal((len(lens), h, d)).astype(np.float32)
+    kc, vc, tables, ctx = _contiguous_to_paged(k_list, v_list, np.float64, rng)
+    kc32, vc32 = kc.astype(np.float32), vc.astype(np.float32)
+    scale = 1.0 / math.sqrt(d)
+    for w in (1, 2, 5, 15, 16, 17, 33, 100, 1000):
+        got = pa.paged_decode(q, "f32", kc32, vc32, "f32", tables, ctx, BS, scale, window=w)
+        for s, n in enumerate(lens):
+            lo = max(0, n - w)
+            k = np.repeat(k_list[s][lo:].astype(np.float32).astype(np.float64), h // hkv, axis=1)
+            v = np.repeat(v_list[s][lo:].astype(np.float32).astype(np.float64), h // hkv, axis=1)
+            want = _sdpa(q[s].astype(np.float64), k, v, scale)
+            np.testing.assert_allclose(got[s], want, rtol=0, atol=1e-12, err_msg=f"W={w} seq {s}")
+
+
+def pin_window_one_and_released_blocks(pa):
+    """W = 1 gives exactly the last token's V row; tokens before the window may
+    hold NaN and whole blocks before it may be released (table entry -1, the
+    allocator model's sliding-window trim) without any effect."""
+    rng = np.random.default_rng(29)
+    hkv, d, n, w = 2, 16, 70, 20
+    alloc = AllocatorModel(12, BS)
+    alloc.set_free_order(rng.permutation(12).tolist())
+    sid = alloc.seq_create()
+    slots, _ = alloc.seq_append_tokens(sid, n)
+    kc = rng.standard_normal((12, BS, hkv, d)).astype(np.float32)
+    vc = rng.standard_normal((12, BS, hkv, d)).astype(np.float32)
+    q = rng.standard_normal((1, hkv, d)).astype(np.float32)
+    tables, lens = alloc.export_block_tables([sid], 6)
+    full = pa.paged_decode(q, "f32", kc, vc, "f32", np.array(tables), lens, BS, 0.3, window=w)
+    last = slots[-1]
+    one = pa.paged_decode(q, "f32", kc, vc, "f32", np.array(tables), lens, BS, 0.3, window=1)
+    assert np.array_equal(one[0], vc.reshape(-1, hkv, d)[last].astype(np.float64))
+    released = alloc.seq_trim_window(sid, w)
+    assert released and all(0 <= b < 12 for b in released)
+    assert sum(1 for b in alloc.seqs[sid]["blocks"] if b >= 0) <= (w + BS - 1) // BS + 1
+    kp, vp = kc.copy(), vc.copy()
+    for slot in slots[: n - w]:
+        kp.reshape(-1, hkv, d)[slot] = np.nan
+        vp.reshape(-1, hkv, d)[slot] = np.nan
+    tables2, lens2 = alloc.export_block_tables([sid], 6)
+    assert tables2[0][0] == -1 and lens2 == lens
+    trimmed = pa.paged_decode(q, "f32", kp, vp, "f32", np.array(tables2), lens2, BS, 0.3, window=w)
+    assert np.array_equal(trimmed, full)
+
+
 ALL_DECODE_PINS = [
     pin_sdpa_contiguous, pin_closed_forms, pin_one_hot, pin_permutation_invariance,
     pin_shared_equals_duplicated, pin_gqa_equals_repeated_mha, pin_unread_slots_ignored,
-    pin_int8_dequant, pin_bf16_decode,
+    pin_int8_dequant, pin_bf16_decode, pin_window_equals_contiguous_tail,
+    pin_window_one_and_released_blocks,
 ]
 ALL_CACHE_WRITE_PINS = [pin_cache_write_float, pin_cache_write_int8]

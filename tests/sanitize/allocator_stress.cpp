@@ -7,6 +7,7 @@
 // sequences, lookups past the allocated blocks) must leave the state
 // unchanged.  At the end every sequence is freed and every count must be 0
 // with the free list a permutation of 0..N-1.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <random>
@@ -27,7 +28,7 @@ namespace {
 
 struct Shadow {
   std::vector<int> refs;
-  struct Seq { int32_t id; std::vector<int32_t> blocks; int tokens; };
+  struct Seq { int32_t id; std::vector<int32_t> blocks; int tokens; int min_window; };
   std::vector<Seq> seqs;
 };
 
@@ -53,11 +54,11 @@ void run(unsigned seed, int nb, int bs, int ops) {
   std::vector<int32_t> slots(4 * bs + 8), ids(nb + 1);
   int32_t cow[2];
   for (int op = 0; op < ops; ++op) {
-    const int kind = static_cast<int>(rng() % 7);
+    const int kind = static_cast<int>(rng() % 8);
     if (kind == 0 || sh.seqs.empty()) {  // new sequence
       int32_t s = -1;
       REQUIRE(pkv_seq_create(a, &s) == PKV_OK);
-      sh.seqs.push_back({s, {}, 0});
+      sh.seqs.push_back({s, {}, 0, 0});
     } else if (kind == 1 || kind == 2) {  // append tokens (may need CoW or fail with OOM)
       auto& q = sh.seqs[rng() % sh.seqs.size()];
       const int n = static_cast<int>(rng() % (3 * bs + 1));
@@ -89,12 +90,14 @@ void run(unsigned seed, int nb, int bs, int ops) {
       auto parent = sh.seqs[rng() % sh.seqs.size()];
       int32_t c = -1;
       REQUIRE(pkv_seq_fork(a, parent.id, &c) == PKV_OK);
-      for (int32_t b : parent.blocks) ++sh.refs[b];
-      sh.seqs.push_back({c, parent.blocks, parent.tokens});
+      for (int32_t b : parent.blocks)
+        if (b >= 0) ++sh.refs[b];
+      sh.seqs.push_back({c, parent.blocks, parent.tokens, parent.min_window});
     } else if (kind == 4) {  // free a sequence
       const size_t i = rng() % sh.seqs.size();
       REQUIRE(pkv_seq_free(a, sh.seqs[i].id) == PKV_OK);
-      for (int32_t b : sh.seqs[i].blocks) --sh.refs[b];
+      for (int32_t b : sh.seqs[i].blocks)
+        if (b >= 0) --sh.refs[b];
       sh.seqs.erase(sh.seqs.begin() + static_cast<long>(i));
     } else if (kind == 5) {  // errors that must change nothing
       int32_t out = 0;
@@ -115,6 +118,24 @@ void run(unsigned seed, int nb, int bs, int ops) {
           break;
         }
       }
+    } else if (kind == 7) {  // sliding-window trim
+      auto& q = sh.seqs[rng() % sh.seqs.size()];
+      const int w = 1 + static_cast<int>(rng() % (3 * bs));
+      std::vector<int32_t> rel(q.blocks.size() + 1);
+      int nrel = -1;
+      REQUIRE(pkv_seq_trim_window(a, q.id, w, rel.data(), static_cast<int>(rel.size()), &nrel) ==
+              PKV_OK);
+      const int first_kept = std::max(0, q.tokens - w) / bs;
+      int k = 0;
+      for (int j = 0; j < first_kept; ++j) {
+        if (q.blocks[j] < 0) continue;
+        REQUIRE(rel[k] == q.blocks[j]);
+        --sh.refs[q.blocks[j]];
+        q.blocks[j] = -1;
+        ++k;
+      }
+      REQUIRE(nrel == k);
+      q.min_window = q.min_window ? std::min(q.min_window, w) : w;
     } else {  // raw block ops: allocate, share, copy-on-write, release
       int32_t b = -1;
       if (pkv_allocate(a, 1, &b) == PKV_OK) {
@@ -160,13 +181,17 @@ void run(unsigned seed, int nb, int bs, int ops) {
         REQUIRE(tables[i * mb + j] ==
                 (j < static_cast<int>(sh.seqs[i].blocks.size()) ? sh.seqs[i].blocks[j] : -1));
     }
-    int bad_s = 0, bad_b = 0;
-    REQUIRE(pkv_validate_tables(tables.data(), lens.data(), static_cast<int>(sid.size()), mb, bs,
-                                nb, &bad_s, &bad_b) == PKV_OK);
+    // each table is valid for decode with the smallest window it was trimmed to
+    for (size_t i = 0; i < sid.size(); ++i) {
+      int bad_s = 0, bad_b = 0;
+      REQUIRE(pkv_validate_tables(tables.data() + i * mb, lens.data() + i, 1, mb, bs, nb,
+                                  sh.seqs[i].min_window, &bad_s, &bad_b) == PKV_OK);
+    }
   }
   for (auto& q : sh.seqs) {
     REQUIRE(pkv_seq_free(a, q.id) == PKV_OK);
-    for (int32_t b : q.blocks) --sh.refs[b];
+    for (int32_t b : q.blocks)
+      if (b >= 0) --sh.refs[b];
   }
   check_counts(a, sh, nb);
   std::vector<int32_t> fl(nb);

@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(lib, name), f"{name} declared in pkv.h but not exported"
     # the binding wraps exactly the declared set
     assert sorted(pkv.EXPORTED) == names
-    assert lib.pkv_abi_version() == 1
+    assert lib.pkv_abi_version() == 2
 
 
 def _header_params():
@@ -90,6 +90,13 @@ def test_workspace_size_and_partition_policy():
     assert pkv.decode_workspace_size(32, 64, 64, 128, 16, 128, 4096) == 0
     assert pkv.decode_partition_size(2, 4, 4, 64, 16, 7, 32) == 32
     assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7, 32) == 2 * 4 * 4 * 66 * 4
+    # a sliding window sizes partitions by the blocks the window can touch,
+    # ceil((W - 1) / 16) + 1, not by the table
+    assert pkv.decode_partition_size(32, 32, 8, 128, 16, 1024, 0, 4096) == 1024   # 257 blocks
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 16, 1024, 0, 4096) == 32 * 32 * 5 * 130 * 4
+    assert pkv.decode_partition_size(64, 32, 8, 128, 16, 1024, 0, 2048) == 0      # 129 blocks
+    assert pkv.decode_workspace_size(64, 32, 8, 128, 16, 1024, 0, 2048) == 0
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 16, 1024, 0, -1) == 0        # invalid
     # not a multiple of the block size -> invalid -> 0
     assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7, 40) == 0
     assert pkv.decode_workspace_size(2, 4, 3, 64, 16, 7) == 0          # 4 % 3 != 0
@@ -98,13 +105,13 @@ def test_workspace_size_and_partition_policy():
 def _decode(lib, **kw):
     args = dict(out=1, q=1, kc=1, vc=1, ks=None, vs=None, tables=1, lens=1, B=2, H=4, Hkv=4,
                 D=64, bs=16, MB=7, NB=32, scale=0.125, qf=pkv.F32, kvf=pkv.F32, part=0,
-                ws=None, wsb=0)
+                win=0, ws=None, wsb=0)
     args.update(kw)
     a = args
     return lib.pkv_paged_attention_decode(
         a["out"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["tables"], a["lens"], a["B"],
         a["H"], a["Hkv"], a["D"], a["bs"], a["MB"], a["NB"], a["scale"], a["qf"], a["kvf"],
-        a["part"], a["ws"], a["wsb"], None)
+        a["part"], a["win"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -124,6 +131,7 @@ def _decode(lib, **kw):
     (dict(part=40), pkv.ERR_INVALID_ARG),
     (dict(part=32), pkv.ERR_WORKSPACE),                     # split needs a workspace
     (dict(part=32, ws=1, wsb=16), pkv.ERR_WORKSPACE),
+    (dict(win=-1), pkv.ERR_INVALID_ARG),
 ])
 def test_decode_rejects_bad_arguments(kw, code):
     lib = pkv.load()
@@ -164,3 +172,8 @@ def test_validate_tables():
     assert pkv.validate_tables(tables, [40, 40], 16, 8) == (0, 2)      # reads the -1 pad
     assert pkv.validate_tables(tables, [20, 40], 16, 7) == (1, 1)      # 7 outside a 7-block pool
     assert pkv.validate_tables(tables, [20, 49], 16, 8) == (1, -1)     # longer than the table
+    # with a sliding window only the window's blocks are read
+    trimmed = np.array([[-1, -1, 5, 6]], np.int32)
+    assert pkv.validate_tables(trimmed, [60], 16, 8, window=20) is None  # tokens 40..59
+    assert pkv.validate_tables(trimmed, [60], 16, 8, window=30) == (0, 1)
+    assert pkv.validate_tables(trimmed, [60], 16, 8) == (0, 0)

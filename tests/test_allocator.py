@@ -120,13 +120,18 @@ def test_differential_against_model(seed):
             op = ["free", "incref"][int(rng.integers(2))]
             if op == "free":
                 # never free blocks a live sequence still owns through its table
-                owned = {b for s in live for b in model.seqs[s]["blocks"]}
+                owned = {b for s in live for b in model.seqs[s]["blocks"] if b >= 0}
                 ids = [i for i in ids if i not in owned] or [nb + 5]
             a, b = _apply(model, op, (ids,)), _apply(lib, op, (ids,))
             assert a[0] == b[0], (step, op, ids, a, b)
             if op == "incref" and a[0] == "ok":
                 model.free(ids)
                 lib.free(ids)
+        elif r == 8 and rng.integers(2):
+            sid = live[rng.integers(len(live))]
+            w = int(rng.integers(0, 5 * bs))
+            a, b = _apply(model, "seq_trim_window", (sid, w)), _apply(lib, "seq_trim_window", (sid, w))
+            assert a == b, (step, a, b)
         elif r == 8:
             sid = live[rng.integers(len(live))]
             tok = int(rng.integers(-2, 4 * bs))
@@ -183,3 +188,29 @@ def test_shared_prefix_config_refcounts():
     pairs = [b.seq_append_tokens(s, 1)[1] for s in kids]
     assert [len(p) for p in pairs] == [1, 1, 1, 0]
     assert b.cow_count() == 3
+
+
+def test_trim_window_keeps_cache_constant():
+    """[P2] sliding window: however long a sequence grows, trimming after each
+    append keeps at most ceil(W / bs) + 1 blocks; released blocks are reused,
+    lookups behind the window are IndexError, export pads them."""
+    bs, w = 16, 40
+    a = pkv.BlockAllocator(8, bs)
+    sid = a.seq_create()
+    for step in range(60):
+        a.seq_append_tokens(sid, 7)
+        a.seq_trim_window(sid, w)
+        held = [b for b in a.seq_block_ids(sid) if b >= 0]
+        assert len(held) <= (w + bs - 1) // bs + 1
+        assert a.num_free() == 8 - len(held)
+    n = a.seq_num_tokens(sid)
+    assert n == 420
+    with pytest.raises(IndexError):
+        a.seq_physical_block(sid, n - w - bs)
+    a.seq_physical_block(sid, n - w)
+    tables, lens = a.export_block_tables([sid], 27, pad=-1)
+    assert (tables[0][: (n - w) // bs] == -1).all() and lens[0] == n
+    with pytest.raises(ValueError):
+        a.seq_trim_window(sid, 0)
+    a.seq_free(sid)
+    assert a.num_free() == 8

@@ -249,3 +249,60 @@ def test_short_contexts_large_values(gpu_lib, kv_fmt, group):
     got = out_f64(gpu_decode(gpu_lib, wl))
     assert_parity(got, oracle_decode(wl), kv_fmt, kv_fmt, with_output_rounding=True,
                   label=f"{kv_fmt} G={group} short contexts")
+
+
+def _behind_window(wl, window):
+    """Copy of the workload whose table entries before each window's first
+    block are -1 (released, as a sliding-window trim leaves them) and whose
+    tokens before the window hold NaN (float) or +-127 (int8) in the cache."""
+    import copy
+    w2 = copy.copy(wl)
+    w2.block_tables = wl.block_tables.copy()
+    w2.key_cache, w2.value_cache = wl.key_cache.copy(), wl.value_cache.copy()
+    for s, n in enumerate(wl.context_lens.tolist()):
+        first = max(0, n - window)
+        for i in range(first):
+            b, o = wl.block_tables[s, i // 16], i % 16
+            for c in (w2.key_cache, w2.value_cache):
+                if wl.kv_fmt == "i8":
+                    c[b, o] = np.int8(127)
+                elif wl.kv_fmt == "bf16":
+                    c[b, o] = np.uint16(0x7FC0)
+                else:
+                    c[b, o] = np.nan
+        w2.block_tables[s, : first // 16] = -1
+    return w2
+
+
+@pytest.mark.parametrize("kv_fmt,q_fmt,group", [("f32", "f32", 1), ("f16", "f16", 1),
+                                                ("bf16", "bf16", 8), ("i8", "f16", 4),
+                                                ("f16", "f16", 16)])
+def test_sliding_window_parity(gpu_lib, kv_fmt, q_fmt, group):
+    """Sliding window W ([P2]): only the last W tokens take part; entries and
+    slots behind the window are released / poisoned and must not be read."""
+    hkv = 2
+    wl = W.make_workload(2, seed=41 + group, num_seqs=5, num_heads=group * hkv, num_kv_heads=hkv,
+                         head_dim=128, kv_fmt=kv_fmt, q_fmt=q_fmt,
+                         ctx=("fixed", [1, 17, 300, 700, 1000]), max_blocks=64,
+                         poison_unused=True)
+    for window in (1, 7, 16, 17, 100, 333, 5000):
+        w2 = _behind_window(wl, window)
+        ref = oracle_decode(w2, window=window)
+        for part in (0, 64):
+            got = out_f64(gpu_decode(gpu_lib, w2, partition_size=part, window=window))
+            assert_parity(got, ref, kv_fmt, q_fmt, with_output_rounding=True,
+                          label=f"{kv_fmt} G={group} W={window} part={part}")
+
+
+def test_sliding_window_one_hot(gpu_lib):
+    """W = 1: the output is exactly the last token's V row, bit for bit."""
+    for group_heads, hkv in ((16, 2), (2, 2)):
+        w = W.make_workload(2, seed=3, num_seqs=4, num_heads=group_heads, num_kv_heads=hkv,
+                            head_dim=128, kv_fmt="bf16", q_fmt="bf16",
+                            ctx=("fixed", [1, 16, 17, 500]), max_blocks=40)
+        out = gpu_decode(gpu_lib, w, window=1)
+        got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        for s, n in enumerate(w.context_lens.tolist()):
+            b, o = w.block_tables[s, (n - 1) // 16], (n - 1) % 16
+            want = np.repeat(w.value_cache[b, o], group_heads // hkv, axis=0)
+            assert np.array_equal(got[s], want), (group_heads, s)

@@ -17,7 +17,10 @@ MUTATIONS = {
     "k_scale_for_v": ("v = v * np.asarray(v_scales", "v = v * np.asarray(k_scales"),
     "scale_index_transposed": ("np.asarray(k_scales, dtype=np.float64)[phys][:, :, None]",
                                "np.asarray(k_scales, dtype=np.float64)[phys][:, None, :].transpose(0, 2, 1)[:, ::-1]"),
-    "off_by_one_context": ("tokens = np.arange(n)", "tokens = np.arange(1, n + 1) if n < 45 else np.arange(n)"),
+    "off_by_one_context": ("tokens = np.arange(start, n)", "tokens = np.arange(start + 1, n + 1) if n < 45 else np.arange(start, n)"),
+    "window_off_by_one": ("start = max(0, n - int(window)) if window else 0", "start = max(0, n - int(window) + 1) if window else 0"),
+    "window_ignored": ("start = max(0, n - int(window)) if window else 0", "start = 0"),
+    "window_from_block_start": ("start = max(0, n - int(window)) if window else 0", "start = max(0, n - int(window)) // block_size * block_size if window else 0"),
     "bf16_wrong_shift": ("<< np.uint32(16)", "<< np.uint32(15)"),
     "v_from_k": ("v = to_f64(value_cache[phys, offset], kv_fmt)", "v = to_f64(key_cache[phys, offset], kv_fmt)"),
     "int8_round_floor": ("code = np.clip(np.rint(x / sc), -127, 127)", "code = np.clip(np.floor(x / sc), -127, 127)"),
