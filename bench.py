@@ -9,8 +9,9 @@ generator, and resident in HBM before the timed region starts.
     python bench.py [--steps K] [--warmup W] [--config 3] [--partition 0]
 
 prints ONE JSON line.  ``value`` is context tokens attended per second over the
-timed steps (sum of context lengths per step x steps / wall time between two
-device synchronisations).  ``roofline`` reports the decode call (the dominant
+timed steps (tokens attended per step, i.e. the context lengths or, with a
+sliding window, min(length, window), x steps / wall time between two device
+synchronisations).  ``roofline`` reports the decode call (the dominant
 kernel) against HBM bandwidth: algorithmic bytes per call (K and V of every
 context token read once, each shared block counted once, plus Q, the output,
 the block-table entries, the lengths and int8 scales) over its average
@@ -52,17 +53,20 @@ def algorithmic_bytes(wl):
     entries and lengths it reads, Q in and the output out."""
     bs = wl.block_size
     row = wl.num_kv_heads * wl.head_dim * ELEM_BYTES[wl.kv_fmt]   # one token, all kv heads
-    valid = {}
+    slots = {}   # physical block -> set of attended offsets
     table_entries = 0
+    logical_tokens = 0
     for s in range(wl.num_seqs):
         n = int(wl.context_lens[s])
-        nb = (n + bs - 1) // bs
-        table_entries += nb
-        for j in range(nb):
+        first = max(0, n - wl.window) if wl.window else 0
+        logical_tokens += n - first
+        for j in range(first // bs, (n + bs - 1) // bs):
+            table_entries += 1
             b = int(wl.block_tables[s, j])
-            valid[b] = max(valid.get(b, 0), min(bs, n - j * bs))
+            lo, hi = max(first - j * bs, 0), min(bs, n - j * bs)
+            slots.setdefault(b, set()).update(range(lo, hi))
+    valid = {b: len(o) for b, o in slots.items()}
     unique_tokens = sum(valid.values())
-    logical_tokens = int(wl.context_lens.sum())
     kv = 2 * unique_tokens * row
     scales = 2 * 4 * wl.num_kv_heads * len(valid) if wl.kv_fmt == "i8" else 0
     qo = 2 * wl.num_seqs * wl.num_heads * wl.head_dim * ELEM_BYTES[wl.q_fmt]
@@ -109,9 +113,10 @@ def cpu_baseline(wl, budget_s):
                                           wl.k_scales, wl.v_scales, in_place=True)
             pa.paged_decode(wl.q[s:s + 1], wl.q_fmt, kc, vc, wl.kv_fmt, wl.block_tables[s:s + 1],
                             wl.context_lens[s:s + 1], wl.block_size, wl.scale, wl.k_scales,
-                            wl.v_scales)
+                            wl.v_scales, window=wl.window)
             spent += time.perf_counter() - t0
-            tokens += int(wl.context_lens[s])
+            n = int(wl.context_lens[s])
+            tokens += min(n, wl.window) if wl.window else n
             done += 1
     return {"value": tokens / spent, "unit": "context tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} sequence decodes ({done / wl.num_seqs:.2f} passes over the "
@@ -126,7 +131,7 @@ def parity_sample(wl, out, n=4, seed=0):
     seqs = np.sort(rng.choice(wl.num_seqs, size=min(n, wl.num_seqs), replace=False))
     ref = pa.paged_decode(wl.q[seqs], wl.q_fmt, wl.key_cache, wl.value_cache, wl.kv_fmt,
                           wl.block_tables[seqs], wl.context_lens[seqs], wl.block_size, wl.scale,
-                          wl.k_scales, wl.v_scales)
+                          wl.k_scales, wl.v_scales, window=wl.window)
     got = out.float().cpu().numpy().astype(np.float64)[seqs]
     return float(np.abs(got - ref).max()), seqs.tolist()
 
@@ -136,7 +141,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3, help="workload 1..5 (default 3: 70B-shaped fp16)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 1..6 (default 3: 70B-shaped fp16; 6: sliding window)")
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = library default)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -185,8 +191,10 @@ def main():
     out = torch.empty_like(q)
     B, H, D = q.shape
     MB = tables.shape[1]
-    part = pkv.decode_partition_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition)
-    need = pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition)
+    part = pkv.decode_partition_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition,
+                                     wl.window)
+    need = pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition,
+                                     wl.window)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -195,7 +203,7 @@ def main():
 
     def decode():
         pkv.paged_attention_decode(out, q, kc, vc, tables, lens, wl.block_size, wl.scale, ks, vs,
-                                   partition_size=args.partition, workspace=ws)
+                                   partition_size=args.partition, workspace=ws, window=wl.window)
 
     for _ in range(args.warmup):
         write()
@@ -258,7 +266,7 @@ def main():
             "head_dim": wl.head_dim, "block_size": wl.block_size, "kv_dtype": wl.kv_fmt,
             "q_dtype": wl.q_fmt, "sum_context_tokens": ctx_per_step,
             "max_blocks_per_seq": MB, "num_blocks": wl.num_blocks,
-            "partition_tokens": part, "seed": wl.seed,
+            "partition_tokens": part, "seed": wl.seed, "sliding_window": wl.window,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

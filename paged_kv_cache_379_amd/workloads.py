@@ -13,6 +13,11 @@ shapes: 64 heads of dimension 128 in FP16 at 2048 tokens and batch 32 (the
 ([P2] "Prefix Cache复用共享前缀的KV Cache") and an INT8 cache ([P2]
 "量化压缩KV Cache的INT8与FP8方案").
 
+A sliding-window workload keeps, per sequence, only the blocks that hold one
+of its last W tokens (the others are released, their table entries -1), as
+[P2] "Sliding Window Attention控制长序列显存" describes for Mistral-7B with
+W = 4096.
+
 Recipe (``np.random.default_rng(seed)``; draw order ctx -> pool permutation
 -> Q -> K -> V -> new K -> new V):
 
@@ -43,6 +48,7 @@ CONFIG_NAMES = {
     3: "llama2_70b_fp16_mha",
     4: "shared_prefix_gqa_bf16",
     5: "high_concurrency_int8_gqa",
+    6: "sliding_window_gqa_bf16",
 }
 
 
@@ -66,6 +72,7 @@ class Workload:
     k_scales: np.ndarray = None   # [NB, Hkv] fp32 (int8 only)
     v_scales: np.ndarray = None
     shared_prefix_blocks: int = 0
+    window: int = 0               # sliding window in tokens (0 = whole context)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -98,7 +105,8 @@ class Workload:
         for s in range(self.num_seqs):
             n = int(self.context_lens[s])
             nb = (n + self.block_size - 1) // self.block_size
-            ids.append(self.block_tables[s, :nb])
+            fb = max(0, n - self.window) // self.block_size if self.window else 0
+            ids.append(self.block_tables[s, fb:nb])
         return np.unique(np.concatenate(ids)) if ids else np.zeros(0, np.int32)
 
 
@@ -171,6 +179,10 @@ def _spec(index):
         return dict(num_seqs=256, num_heads=32, num_kv_heads=8, head_dim=128,
                     kv_fmt="i8", q_fmt="f16", ctx=("lognormal", 512, 0.8, 4096),
                     pool=("factor", 1.25), max_blocks=256, prefix=0)
+    if index == 6:
+        return dict(num_seqs=32, num_heads=32, num_kv_heads=8, head_dim=128,
+                    kv_fmt="bf16", q_fmt="bf16", ctx=("uniform", 4096, 16384),
+                    pool=("factor", 1.25), max_blocks=1024, prefix=0, window=4096)
     raise ValueError(f"no configuration {index}")
 
 
@@ -191,9 +203,16 @@ def _draw_structure(cfg, rng, bs):
     prefix_tokens = int(cfg["prefix"])
     prefix_blocks = prefix_tokens // bs if prefix_tokens else 0
     blocks_per_seq = (lens.astype(np.int64) + bs - 1) // bs
+    # With a sliding window only the blocks that hold one of the last `window`
+    # tokens are kept; the table entries before them are -1 (released).
+    window = int(cfg.get("window", 0))
+    if window and prefix_tokens:
+        raise ValueError("a shared prefix and a sliding window are not combined")
+    first_block = (np.maximum(lens.astype(np.int64) - window, 0) // bs if window
+                   else np.zeros(B, dtype=np.int64))
     if prefix_tokens and lens.min() <= prefix_tokens:
         raise ValueError("every sequence must extend past the shared prefix")
-    own_blocks = blocks_per_seq - prefix_blocks
+    own_blocks = blocks_per_seq - prefix_blocks - first_block
     needed = int(prefix_blocks + own_blocks.sum())
     if cfg["pool"][0] == "fixed":
         nb = int(cfg["pool"][1])
@@ -215,7 +234,8 @@ def _draw_structure(cfg, rng, bs):
     for s in range(B):
         tables[s, :prefix_blocks] = shared
         n_own = int(own_blocks[s])
-        tables[s, prefix_blocks:prefix_blocks + n_own] = handout[pos:pos + n_own]
+        lo = prefix_blocks + int(first_block[s])
+        tables[s, lo:lo + n_own] = handout[pos:pos + n_own]
         pos += n_own
     return dict(lens=lens, tables=tables, num_blocks=nb, prefix_blocks=prefix_blocks,
                 free_list=free_list, blocks_needed=needed)
@@ -231,8 +251,8 @@ def make_structure(index, seed=None, block_size=BLOCK_SIZE, **overrides):
 def make_workload(index, seed=None, *, num_seqs=None, num_heads=None,
                   num_kv_heads=None, head_dim=None, ctx=None, prefix=None,
                   max_blocks=None, kv_fmt=None, q_fmt=None, block_size=BLOCK_SIZE,
-                  poison_unused=False, pool=None):
-    """Draw configuration ``index`` (1..5) with optional overrides.
+                  poison_unused=False, pool=None, window=None):
+    """Draw configuration ``index`` (1..6) with optional overrides.
 
     Overrides shrink or reshape a configuration for parity tests while keeping
     its structure (length mix, sharing, formats).  ``poison_unused`` fills every
@@ -243,7 +263,7 @@ def make_workload(index, seed=None, *, num_seqs=None, num_heads=None,
     cfg = _config(index, dict(num_seqs=num_seqs, num_heads=num_heads,
                               num_kv_heads=num_kv_heads, head_dim=head_dim,
                               kv_fmt=kv_fmt, q_fmt=q_fmt, ctx=ctx, prefix=prefix,
-                              max_blocks=max_blocks, pool=pool))
+                              max_blocks=max_blocks, pool=pool, window=window))
     if seed is None:
         seed = index - 1
     rng = np.random.default_rng(seed)
@@ -277,7 +297,7 @@ def make_workload(index, seed=None, *, num_seqs=None, num_heads=None,
         kv_fmt=kv_fmt_, block_tables=tables, context_lens=lens, block_size=bs,
         scale=1.0 / math.sqrt(D), k_new=k_new, v_new=v_new, new_fmt=new_fmt,
         slot_mapping=slots, k_scales=k_scales, v_scales=v_scales,
-        shared_prefix_blocks=st["prefix_blocks"],
+        shared_prefix_blocks=st["prefix_blocks"], window=int(cfg.get("window", 0)),
         extra={"free_list": st["free_list"], "blocks_needed": st["blocks_needed"]},
     )
     if poison_unused:
@@ -286,14 +306,14 @@ def make_workload(index, seed=None, *, num_seqs=None, num_heads=None,
 
 
 def used_slot_mask(wl):
-    """Boolean [NB, bs]: True where some sequence's context reads the slot."""
+    """Boolean [NB, bs]: True where some sequence's context (its window, if the
+    workload has one) reads the slot."""
     used = np.zeros((wl.num_blocks, wl.block_size), dtype=bool)
     for s in range(wl.num_seqs):
         n = int(wl.context_lens[s])
-        full, rem = divmod(n, wl.block_size)
-        used[wl.block_tables[s, :full]] = True
-        if rem:
-            used[wl.block_tables[s, full], :rem] = True
+        first = max(0, n - wl.window) if wl.window else 0
+        for i in range(first, n):
+            used[wl.block_tables[s, i // wl.block_size], i % wl.block_size] = True
     return used
 
 

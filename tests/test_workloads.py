@@ -103,3 +103,24 @@ def test_bf16_rounding_matches_torch():
     bits = W._round_to(x, "bf16")
     want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(bits, want)
+
+
+def test_sliding_window_workload_structure():
+    """Config 6: only the blocks holding one of the last W tokens are allocated
+    (distinct ids from the pool), every earlier entry is -1, and the cache
+    held per sequence is the constant ceil((W - 1) / 16) + 1 blocks or fewer."""
+    st = W.make_structure(6)
+    lens, tables, w = st["lens"], st["tables"], 4096
+    held = []
+    for s, n in enumerate(lens.tolist()):
+        first_block = max(0, n - w) // 16
+        nb = (n + 15) // 16
+        assert (tables[s, :first_block] == -1).all()
+        assert (tables[s, first_block:nb] >= 0).all() and (tables[s, nb:] == -1).all()
+        held.append(tables[s, first_block:nb])
+        assert nb - first_block <= (w - 1 + 15) // 16 + 1
+    ids = np.concatenate(held)
+    assert len(np.unique(ids)) == len(ids) and ids.max() < st["num_blocks"]
+    wl = W.make_workload(6, num_seqs=2, poison_unused=True)
+    used = W.used_slot_mask(wl)
+    assert used.sum() == sum(min(int(n), w) for n in wl.context_lens)
