@@ -8,7 +8,8 @@ generator, and resident in HBM before the timed region starts.
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--partition 0]
 
-prints ONE JSON line.  ``value`` is context tokens attended per second over the
+prints ONE JSON line (``--swap`` measures preemption instead: swapping KV
+blocks to pinned host memory and back, and batched copy-on-write copies).  ``value`` is context tokens attended per second over the
 timed steps (tokens attended per step, i.e. the context lengths or, with a
 sliding window, min(length, window), x steps / wall time between two device
 synchronisations).  ``roofline`` reports the decode call (the dominant
@@ -136,6 +137,113 @@ def parity_sample(wl, out, n=4, seed=0):
     return float(np.abs(got - ref).max()), seqs.tolist()
 
 
+PCIE_PEAK_GBPS = 64.0   # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
+
+
+def swap_bench(args, torch, pkv, log):
+    """Preemption on the 70B-shaped fp16 pool: swap 8 sequences of 2048 tokens
+    out to pinned host memory and back in through the allocator's pair lists,
+    and copy-on-write one partly filled block for each of 32 forked sequences.
+    Prints one JSON line."""
+    dev = torch.device("cuda:0")
+    bs, hkv, d, n_pre, ctx = 16, 64, 128, 8, 2048
+    nb = 4096                         # 2 GiB of K and V
+    blocks = n_pre * ctx // bs
+    nhb = blocks
+    shape = (nb, bs, hkv, d)
+    kc = torch.randn(shape, dtype=torch.float16, device=dev)
+    vc = torch.randn(shape, dtype=torch.float16, device=dev)
+    hk = torch.empty((nhb,) + shape[1:], dtype=torch.float16, pin_memory=True)
+    hv = torch.empty((nhb,) + shape[1:], dtype=torch.float16, pin_memory=True)
+    block_bytes = bs * hkv * d * 2
+    a = pkv.BlockAllocator(nb, bs)
+    a.set_free_order(np.random.default_rng(0).permutation(nb))
+    a.set_host_pool(nhb)
+    seqs = []
+    for _ in range(n_pre):
+        s = a.seq_create()
+        a.seq_append_tokens(s, ctx)
+        seqs.append(s)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    out_us, in_us, host_us = [], [], []
+    for rep in range(args.warmup + args.steps):
+        t = time.perf_counter()
+        out_pairs = [p for s in seqs for p in a.seq_swap_out(s)]
+        t_out = time.perf_counter() - t
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record()
+        pkv.swap_blocks(kc, vc, hk, hv, out_pairs, pkv.SWAP_OUT)
+        e1.record()
+        t = time.perf_counter()
+        in_pairs = [p for s in seqs for p in a.seq_swap_in(s)]
+        t_in = time.perf_counter() - t
+        pkv.swap_blocks(kc, vc, hk, hv, in_pairs, pkv.SWAP_IN)
+        e2.record()
+        torch.cuda.synchronize()
+        if rep >= args.warmup:
+            out_us.append(e0.elapsed_time(e1) * 1e3)
+            in_us.append(e1.elapsed_time(e2) * 1e3)
+            host_us.append((t_out + t_in) * 1e6 / 2)
+    moved = 2 * blocks * block_bytes
+    out_gbps = moved / (np.mean(out_us) * 1e-6) / 1e9
+    in_gbps = moved / (np.mean(in_us) * 1e-6) / 1e9
+    # Reference: one contiguous DMA copy of the same size each way.
+    flat = kc.view(-1)[: moved // 2]
+    pinned = torch.empty(moved // 2, dtype=torch.float16, pin_memory=True)
+    dma = {}
+    for name, fn in (("d2h", lambda: pinned.copy_(flat, non_blocking=True)),
+                     ("h2d", lambda: flat.copy_(pinned, non_blocking=True))):
+        fn()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(3):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        dma[name] = moved * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    # Batched copy-on-write: 32 forks of a 2056-token prompt append one token each.
+    cow_a = pkv.BlockAllocator(nb, bs)
+    root = cow_a.seq_create()
+    cow_a.seq_append_tokens(root, 2056)
+    cow_pairs = []
+    for _ in range(32):
+        c = cow_a.seq_fork(root)
+        cow_pairs += cow_a.seq_append_tokens(c, 1)[1]
+    pkv.copy_blocks(kc, vc, cow_pairs)
+    e0, e1 = ev(), ev()
+    e0.record()
+    for _ in range(args.steps):
+        pkv.copy_blocks(kc, vc, cow_pairs)
+    e1.record()
+    torch.cuda.synchronize()
+    cow_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    log(f"swap out {np.mean(out_us):.0f} us ({out_gbps:.1f} GB/s), in {np.mean(in_us):.0f} us "
+        f"({in_gbps:.1f} GB/s); DMA probe d2h {dma['d2h']:.1f} h2d {dma['h2d']:.1f} GB/s; "
+        f"CoW of {len(cow_pairs)} blocks {cow_us:.1f} us")
+    result = {
+        "metric": "preemption swap: KV bytes moved between HBM and pinned host memory per second",
+        "value": 2 * moved / ((np.mean(out_us) + np.mean(in_us)) * 1e-6),
+        "unit": "B/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": (np.mean(out_us) + np.mean(in_us)) / 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "swap_llama2_70b_fp16", "preempted_seqs": n_pre,
+                   "tokens_per_seq": ctx, "block_size": bs, "num_kv_heads": hkv, "head_dim": d,
+                   "blocks_swapped": blocks, "block_bytes_k_plus_v": 2 * block_bytes},
+        "roofline": {"bound": "pcie", "achieved": (out_gbps + in_gbps) / 2, "peak": PCIE_PEAK_GBPS,
+                     "unit": "GB/s", "frac": (out_gbps + in_gbps) / 2 / PCIE_PEAK_GBPS,
+                     "traffic": None, "kernel": "copy_blocks_kernel"},
+        "swap_out_us": float(np.mean(out_us)), "swap_in_us": float(np.mean(in_us)),
+        "swap_out_gbps": out_gbps, "swap_in_gbps": in_gbps,
+        "dma_probe_gbps": dma, "allocator_us_per_swap_call_set": float(np.mean(host_us)),
+        "cow_blocks": len(cow_pairs), "cow_copy_us": cow_us,
+        "cow_gbps": 2 * len(cow_pairs) * 2 * block_bytes / (cow_us * 1e-6) / 1e9,
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +256,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure preemption instead: swap-out/in over PCIe and batched CoW copies")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -168,6 +278,10 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.swap:
+        swap_bench(args, torch, pkv, log)
+        return
 
     t = time.perf_counter()
     wl = W.make_workload(args.config, seed=args.seed)

@@ -13,7 +13,8 @@
  *   - Device buffers are owned by the caller (the library never allocates,
  *     frees or synchronises device memory, except that pkv_copy_blocks takes
  *     its pairs from host memory).  Host buffers are only read or written during
- *     the call.
+ *     the call, except the pinned host pools of pkv_swap_blocks, which its
+ *     kernel reads and writes on the stream.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Kernels are enqueued on it; functions return before they finish.
  *   - Shapes and sizes are validated on the host.  Values that live in device
@@ -192,6 +193,40 @@ int pkv_copy_blocks(void* key_cache, void* value_cache, float* k_scales,
                     void* stream);
 
 /*
+ * Swap whole blocks between the device pool and a pool of host blocks
+ * ([P1] "vLLM调度器与PagedAttention协同工作", preemption and recovery: when
+ * device memory runs short a low-priority request's KV moves to CPU memory,
+ * freeing its device blocks, and is copied back once blocks are free again;
+ * [P1] deployment section, swap_space).
+ *
+ *   key_cache, value_cache, k_scales, v_scales  the device pool (layout above;
+ *                scales NULL for float caches, else fp32 [num_blocks][scale_stride])
+ *   host_key, host_value  PINNED host memory allocated with hipHostMalloc (or a
+ *                pinned torch tensor), [num_host_blocks][block_bytes]: block h
+ *                at byte h * block_bytes, the same bytes a device block holds
+ *   host_k_scales, host_v_scales  pinned host fp32 [num_host_blocks][scale_stride],
+ *                NULL exactly when k_scales is
+ *   pairs        HOST int32 pairs, n_pairs of them, as pkv_seq_swap_out and
+ *                pkv_seq_swap_in return them:
+ *                  direction PKV_SWAP_OUT: (device block, host block), device -> host
+ *                  direction PKV_SWAP_IN:  (host block, device block), host -> device
+ *                destination ids distinct; a source may repeat
+ *
+ * The copy is one kernel that reads and writes the pinned memory through its
+ * device mapping (no per-block DMA requests).  It is enqueued on `stream`;
+ * synchronise before the host reads host blocks written by a swap-out, and
+ * keep the source blocks unchanged until the copy has finished.
+ * Errors: INVALID_ARG (ids out of range, repeated destinations, host memory
+ * that is not pinned), HIP.
+ */
+enum { PKV_SWAP_OUT = 0, PKV_SWAP_IN = 1 };
+int pkv_swap_blocks(void* key_cache, void* value_cache, float* k_scales, float* v_scales,
+                    void* host_key, void* host_value, float* host_k_scales,
+                    float* host_v_scales, const int32_t* pairs, int n_pairs,
+                    size_t block_bytes, int num_blocks, int num_host_blocks,
+                    int scale_stride, int direction, void* stream);
+
+/*
  * Plain device-to-device streaming copy of `bytes` bytes (a multiple of 16,
  * 16-byte aligned pointers) with the library's own kernel: the reference
  * point for achievable HBM bandwidth and for scaling hardware byte counters.
@@ -273,13 +308,48 @@ int pkv_seq_append_tokens(pkv_allocator* a, int32_t seq, int n, int32_t* slots_o
  */
 int pkv_seq_trim_window(pkv_allocator* a, int32_t seq, int window, int32_t* released,
                         int cap, int* n_released);
-/* Release all of the sequence's block references and forget it. */
+/*
+ * Swap pool ([P1] "vLLM调度器与PagedAttention协同工作", preemption and
+ * recovery; [P1] deployment section, swap_space in GB).  The allocator also
+ * tracks num_host_blocks host blocks (ids 0..num_host_blocks-1, a LIFO free
+ * list like the device pool's, the first taken is num_host_blocks-1).  Legal
+ * only while no sequence is swapped out; a new size resets the host free list.
+ */
+int pkv_allocator_set_host_pool(pkv_allocator* a, int num_host_blocks);
+int pkv_host_num_free(const pkv_allocator* a, int* out);
+/*
+ * Preempt a sequence: each of its blocks (entries -1 after a trim stay -1)
+ * takes a host block, and the sequence drops its device reference (a block
+ * it shared stays with the other sequences; a block it alone held returns to
+ * the free list).  Its table then holds host ids and the sequence is
+ * "swapped out": append, fork, trim, lookup and export of it fail with
+ * INVALID_ARG until pkv_seq_swap_in.  pairs: host int32[2 * cap] receiving
+ * (device block, host block) in logical order, for pkv_swap_blocks with
+ * PKV_SWAP_OUT, to be enqueued BEFORE any write into the released device
+ * blocks.  *n_pairs = the number of pairs needed, set also on failure.
+ * All or nothing: OOM if the host pool is short, INVALID_ARG if cap is too
+ * small or the sequence is already swapped out.
+ */
+int pkv_seq_swap_out(pkv_allocator* a, int32_t seq, int32_t* pairs, int cap, int* n_pairs);
+/*
+ * Bring a swapped-out sequence back: each host block takes a fresh device
+ * block (reference count 1; sharing from before the swap-out is not restored)
+ * and returns to the host free list.  pairs receives (host block, device
+ * block) for pkv_swap_blocks with PKV_SWAP_IN.  All or nothing: OOM if too
+ * few device blocks are free; INVALID_ARG if cap is too small or the sequence
+ * is not swapped out.
+ */
+int pkv_seq_swap_in(pkv_allocator* a, int32_t seq, int32_t* pairs, int cap, int* n_pairs);
+int pkv_seq_is_swapped(const pkv_allocator* a, int32_t seq, int* out);
+/* Release all of the sequence's block references (host blocks if it is
+ * swapped out) and forget it. */
 int pkv_seq_free(pkv_allocator* a, int32_t seq);
 int pkv_seq_num_tokens(const pkv_allocator* a, int32_t seq, int* out);
-/* The sequence's logical block table (-1 for blocks released by a trim). */
+/* The sequence's logical block table (-1 for blocks released by a trim; host
+ * block ids while it is swapped out). */
 int pkv_seq_block_ids(const pkv_allocator* a, int32_t seq, int32_t* out, int cap, int* n);
 /* Physical block of a logical token ([P3] BlockTable lookup): INDEX if the
- * token's logical block has not been allocated. */
+ * token's logical block has not been allocated; INVALID_ARG if swapped out. */
 int pkv_seq_physical_block(const pkv_allocator* a, int32_t seq, int token, int32_t* out);
 /*
  * Export host block tables for a batch: out_tables int32[n][max_blocks]

@@ -29,7 +29,17 @@ in extraction; the readings taken here:
 * looking up a token whose logical block has not been allocated (or has
   been released behind a sliding window) raises IndexError;
 * ``seq_trim_window`` releases the blocks entirely before the last W tokens
-  ([P2] sliding window section); their table entries read -1.
+  ([P2] sliding window section); their table entries read -1;
+* preemption ([P1] scheduler section, item 3: under memory pressure a
+  low-priority request's KV goes to CPU memory, its device blocks are freed,
+  and it comes back when blocks are free again; [P1] deployment section,
+  swap_space): a host pool of ``num_host_blocks`` blocks with its own LIFO free
+  list.  ``seq_swap_out`` gives each of the sequence's blocks a host block, in
+  logical order, and drops the sequence's device reference (a block other
+  sequences share stays theirs); ``seq_swap_in`` gives each host block a fresh
+  device block (count 1: sharing is not restored) and returns the host block.
+  Both are all or nothing.  A swapped-out sequence cannot be appended to,
+  forked, trimmed, looked up or exported.
 """
 
 
@@ -52,6 +62,8 @@ class AllocatorModel:
         self.seqs = {}          # seq id -> {"blocks": [...], "tokens": int}
         self.next_seq = 0
         self.cow_copies = 0
+        self.num_host_blocks = 0
+        self.host_free = []
 
     # ---- block level -------------------------------------------------------
     def set_free_order(self, order):
@@ -124,16 +136,22 @@ class AllocatorModel:
     def seq_create(self):
         sid = self.next_seq
         self.next_seq += 1
-        self.seqs[sid] = {"blocks": [], "tokens": 0}
+        self.seqs[sid] = {"blocks": [], "tokens": 0, "swapped": False}
         return sid
 
+    def _resident(self, sid):
+        seq = self.seqs[sid]
+        if seq["swapped"]:
+            raise ValueError(f"sequence {sid} is swapped out")
+        return seq
+
     def seq_fork(self, sid):
-        parent = self.seqs[sid]
+        parent = self._resident(sid)
         self.incref([b for b in parent["blocks"] if b >= 0])
         cid = self.next_seq
         self.next_seq += 1
         self.seqs[cid] = {"blocks": list(parent["blocks"]),
-                          "tokens": parent["tokens"]}
+                          "tokens": parent["tokens"], "swapped": False}
         return cid
 
     def seq_append_tokens(self, sid, n):
@@ -146,7 +164,7 @@ class AllocatorModel:
         All or nothing: if the free list cannot cover every block the call
         needs, nothing changes.
         """
-        seq = self.seqs[sid]
+        seq = self._resident(sid)
         bs = self.block_size
         tokens = seq["tokens"]
         need = 0
@@ -178,7 +196,7 @@ class AllocatorModel:
         Their table entries become -1; returns the released ids in order."""
         if window <= 0:
             raise ValueError("window must be positive")
-        seq = self.seqs[sid]
+        seq = self._resident(sid)
         first_kept = max(0, seq["tokens"] - window) // self.block_size
         released = []
         for j in range(first_kept):
@@ -189,12 +207,62 @@ class AllocatorModel:
         self.free(released)
         return released
 
+    def set_host_pool(self, num_host_blocks):
+        if num_host_blocks < 0:
+            raise ValueError("negative host pool")
+        if any(s["swapped"] for s in self.seqs.values()):
+            raise ValueError("a sequence is swapped out")
+        self.num_host_blocks = num_host_blocks
+        self.host_free = list(range(num_host_blocks))
+
+    def seq_swap_out(self, sid):
+        """Returns the (device block, host block) pairs to copy, in logical order."""
+        seq = self._resident(sid)
+        held = [b for b in seq["blocks"] if b >= 0]
+        if len(held) > len(self.host_free):
+            raise OutOfBlocks(f"need {len(held)} host blocks, {len(self.host_free)} free")
+        pairs = []
+        for j, b in enumerate(seq["blocks"]):
+            if b < 0:
+                continue
+            h = self.host_free.pop()
+            pairs.append((b, h))
+            self.free([b])
+            seq["blocks"][j] = h
+        seq["swapped"] = True
+        return pairs
+
+    def seq_swap_in(self, sid):
+        """Returns the (host block, device block) pairs to copy, in logical order."""
+        seq = self.seqs[sid]
+        if not seq["swapped"]:
+            raise ValueError(f"sequence {sid} is not swapped out")
+        held = [h for h in seq["blocks"] if h >= 0]
+        if len(held) > len(self.free_blocks):
+            raise OutOfBlocks(f"need {len(held)} blocks, {len(self.free_blocks)} free")
+        pairs = []
+        for j, h in enumerate(seq["blocks"]):
+            if h < 0:
+                continue
+            d = self.allocate(1)[0]
+            pairs.append((h, d))
+            self.host_free.append(h)
+            seq["blocks"][j] = d
+        seq["swapped"] = False
+        return pairs
+
+    def seq_is_swapped(self, sid):
+        return self.seqs[sid]["swapped"]
+
     def seq_free(self, sid):
         seq = self.seqs.pop(sid)
-        self.free([b for b in seq["blocks"] if b >= 0])
+        if seq["swapped"]:
+            self.host_free.extend(h for h in seq["blocks"] if h >= 0)
+        else:
+            self.free([b for b in seq["blocks"] if b >= 0])
 
     def seq_physical_block(self, sid, token):
-        seq = self.seqs[sid]
+        seq = self._resident(sid)
         idx = token // self.block_size
         if token < 0 or idx >= len(seq["blocks"]) or seq["blocks"][idx] < 0:
             raise IndexError(f"token {token}: block {idx} not allocated")
@@ -203,7 +271,7 @@ class AllocatorModel:
     def export_block_tables(self, sids, max_blocks, pad=-1):
         tables, lens = [], []
         for sid in sids:
-            seq = self.seqs[sid]
+            seq = self._resident(sid)
             if len(seq["blocks"]) > max_blocks:
                 raise ValueError("max_blocks smaller than a sequence's table")
             row = [b if b >= 0 else pad for b in seq["blocks"]]

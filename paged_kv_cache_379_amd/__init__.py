@@ -16,8 +16,8 @@ import numpy as np
 __all__ = [
     "load", "LIB_PATH", "PkvError", "OutOfBlocks", "DoubleFree",
     "paged_attention_decode", "decode_workspace_size", "decode_partition_size",
-    "reshape_and_cache", "copy_blocks", "stream_copy", "validate_tables",
-    "BlockAllocator", "F32", "F16", "BF16", "I8",
+    "reshape_and_cache", "copy_blocks", "swap_blocks", "stream_copy", "validate_tables",
+    "BlockAllocator", "F32", "F16", "BF16", "I8", "SWAP_OUT", "SWAP_IN",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 # Status codes and formats (include/pkv.h).
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OOM, ERR_DOUBLE_FREE, ERR_INDEX, ERR_HIP, ERR_WORKSPACE = range(8)
 F32, F16, BF16, I8 = 0, 1, 2, 3
+SWAP_OUT, SWAP_IN = 0, 1
 
 
 class PkvError(RuntimeError):
@@ -54,6 +55,7 @@ _SIGS = {
                                    + [_vp, _c_size, _vp]),
     "pkv_reshape_and_cache": (_c_int, [_vp] * 7 + [_c_int] * 7 + [_vp]),
     "pkv_copy_blocks": (_c_int, [_vp] * 4 + [_i32p, _c_int, _c_size, _c_int, _c_int, _vp]),
+    "pkv_swap_blocks": (_c_int, [_vp] * 8 + [_i32p, _c_int, _c_size] + [_c_int] * 4 + [_vp]),
     "pkv_stream_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
     "pkv_allocator_create": (_c_int, [_c_int, _c_int, ctypes.POINTER(_vp)]),
     "pkv_allocator_destroy": (_c_int, [_vp]),
@@ -72,6 +74,11 @@ _SIGS = {
     "pkv_seq_append_tokens": (_c_int, [_vp, ctypes.c_int32, _c_int, _i32p, _i32p, _c_int,
                                        ctypes.POINTER(_c_int)]),
     "pkv_seq_trim_window": (_c_int, [_vp, ctypes.c_int32, _c_int, _i32p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_allocator_set_host_pool": (_c_int, [_vp, _c_int]),
+    "pkv_host_num_free": (_c_int, [_vp, ctypes.POINTER(_c_int)]),
+    "pkv_seq_swap_out": (_c_int, [_vp, ctypes.c_int32, _i32p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_seq_swap_in": (_c_int, [_vp, ctypes.c_int32, _i32p, _c_int, ctypes.POINTER(_c_int)]),
+    "pkv_seq_is_swapped": (_c_int, [_vp, ctypes.c_int32, ctypes.POINTER(_c_int)]),
     "pkv_seq_free": (_c_int, [_vp, ctypes.c_int32]),
     "pkv_seq_num_tokens": (_c_int, [_vp, ctypes.c_int32, ctypes.POINTER(_c_int)]),
     "pkv_seq_block_ids": (_c_int, [_vp, ctypes.c_int32, _i32p, _c_int, ctypes.POINTER(_c_int)]),
@@ -232,6 +239,57 @@ def copy_blocks(key_cache, value_cache, pairs, k_scales=None, v_scales=None, str
     _check(rc)
 
 
+def _pinned_ptr(t, name, like, dtype=None):
+    """Pointer of a pinned host tensor whose rows have the shape of ``like``'s rows."""
+    if t is None:
+        return None
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor (pin_memory=True)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != (dtype or like.dtype) or tuple(t.shape[1:]) != tuple(like.shape[1:]):
+        raise ValueError(f"{name} must have rows like {tuple(like.shape[1:])} {like.dtype}, "
+                         f"got {tuple(t.shape)} {t.dtype}")
+    return t.data_ptr()
+
+
+def swap_blocks(key_cache, value_cache, host_key, host_value, pairs, direction,
+                k_scales=None, v_scales=None, host_k_scales=None, host_v_scales=None,
+                stream=None):
+    """Copy whole blocks between the device pool and a pinned host pool.
+
+    ``pairs`` (host ints) are (device, host) for ``SWAP_OUT`` and (host,
+    device) for ``SWAP_IN``, as :meth:`BlockAllocator.seq_swap_out` and
+    :meth:`BlockAllocator.seq_swap_in` return them.  ``host_key`` and
+    ``host_value`` are pinned tensors [num_host_blocks, bs, Hkv, D] of the
+    cache's dtype; int8 caches also pass their scales and pinned host scales
+    [num_host_blocks, Hkv].
+    """
+    torch = _torch()
+    lib = load()
+    arr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    NB = key_cache.shape[0]
+    NHB = host_key.shape[0]
+    if host_value.shape != host_key.shape:
+        raise ValueError("host_key and host_value differ in shape")
+    if tuple(value_cache.shape) != tuple(key_cache.shape) or value_cache.dtype != key_cache.dtype:
+        raise ValueError("key_cache and value_cache differ")
+    for t, n, name in ((k_scales, NB, "k_scales"), (v_scales, NB, "v_scales"),
+                       (host_k_scales, NHB, "host_k_scales"), (host_v_scales, NHB, "host_v_scales")):
+        if t is not None and (t.dim() != 2 or t.shape[0] != n or t.shape[1] != key_cache.shape[2]):
+            raise ValueError(f"{name} must be [{n}, {key_cache.shape[2]}]")
+    block_bytes = key_cache[0].numel() * key_cache.element_size()
+    rc = lib.pkv_swap_blocks(
+        _dev_ptr(key_cache, "key_cache"), _dev_ptr(value_cache, "value_cache"),
+        _dev_ptr(k_scales, "k_scales", torch.float32), _dev_ptr(v_scales, "v_scales", torch.float32),
+        _pinned_ptr(host_key, "host_key", key_cache), _pinned_ptr(host_value, "host_value", value_cache),
+        _pinned_ptr(host_k_scales, "host_k_scales", k_scales, torch.float32) if k_scales is not None else None,
+        _pinned_ptr(host_v_scales, "host_v_scales", v_scales, torch.float32) if v_scales is not None else None,
+        arr.ctypes.data_as(_i32p), len(arr), block_bytes, NB, NHB, key_cache.shape[2], direction,
+        _stream(stream))
+    _check(rc)
+
+
 def stream_copy(dst, src, nbytes=None, stream=None):
     """The library's streaming copy kernel (bandwidth reference)."""
     lib = load()
@@ -359,6 +417,34 @@ class BlockAllocator:
         _check(self._lib.pkv_seq_trim_window(self._h, seq, window, out.ctypes.data_as(_i32p),
                                              cap, ctypes.byref(n)))
         return out[:n.value].tolist()
+
+    def set_host_pool(self, num_host_blocks):
+        _check(self._lib.pkv_allocator_set_host_pool(self._h, num_host_blocks))
+
+    def host_num_free(self):
+        out = ctypes.c_int()
+        _check(self._lib.pkv_host_num_free(self._h, ctypes.byref(out)))
+        return out.value
+
+    def _swap(self, fn, seq):
+        cap = len(self.seq_block_ids(seq))
+        out = np.empty((max(cap, 1), 2), dtype=np.int32)
+        n = ctypes.c_int()
+        _check(fn(self._h, seq, out.ctypes.data_as(_i32p), cap, ctypes.byref(n)))
+        return [tuple(int(x) for x in r) for r in out[:n.value]]
+
+    def seq_swap_out(self, seq):
+        """Preempt ``seq``; returns the (device, host) block pairs to copy out."""
+        return self._swap(self._lib.pkv_seq_swap_out, seq)
+
+    def seq_swap_in(self, seq):
+        """Resume ``seq``; returns the (host, device) block pairs to copy in."""
+        return self._swap(self._lib.pkv_seq_swap_in, seq)
+
+    def seq_is_swapped(self, seq):
+        out = ctypes.c_int()
+        _check(self._lib.pkv_seq_is_swapped(self._h, seq, ctypes.byref(out)))
+        return bool(out.value)
 
     def seq_free(self, seq):
         _check(self._lib.pkv_seq_free(self._h, seq))

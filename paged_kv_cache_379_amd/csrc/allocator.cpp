@@ -28,8 +28,9 @@
 namespace {
 
 struct Sequence {
-  std::vector<int32_t> blocks;  // logical block -> physical block
+  std::vector<int32_t> blocks;  // logical block -> physical block (host block when swapped)
   int64_t tokens = 0;
+  bool swapped = false;         // blocks live in the host pool
 };
 
 }  // namespace
@@ -42,6 +43,10 @@ struct pkv_allocator {
   std::unordered_map<int32_t, Sequence> seqs;
   int32_t next_seq = 0;
   int64_t cow_copies = 0;
+  // Host (swap) pool: blocks of the same size in pinned host memory.  A
+  // swapped-out sequence owns its host blocks alone, so they need no counts.
+  int num_host_blocks = 0;
+  std::vector<int32_t> host_free;  // the next block to leave is at the back
 
   bool valid_id(int32_t id) const { return id >= 0 && id < num_blocks; }
 
@@ -69,6 +74,13 @@ int find_seq(const pkv_allocator* a, int32_t seq, const Sequence** out) {
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return pkv::fail(PKV_ERR_INVALID_ARG, "no sequence %d", seq);
   *out = &it->second;
+  return PKV_OK;
+}
+
+// A sequence whose blocks are on the device (not swapped out).
+int find_resident(const pkv_allocator* a, int32_t seq, const Sequence** out) {
+  if (int rc = find_seq(a, seq, out)) return rc;
+  if ((*out)->swapped) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d is swapped out", seq);
   return PKV_OK;
 }
 
@@ -245,7 +257,7 @@ int pkv_seq_fork(pkv_allocator* a, int32_t seq, int32_t* child) {
   if (int rc = check_alloc(a)) return rc;
   if (!child) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL output");
   const Sequence* parent;
-  if (int rc = find_seq(a, seq, &parent)) return rc;
+  if (int rc = find_resident(a, seq, &parent)) return rc;
   if (a->next_seq == INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence ids exhausted");
   Sequence copy = *parent;
   for (int32_t b : copy.blocks)
@@ -263,6 +275,7 @@ int pkv_seq_append_tokens(pkv_allocator* a, int32_t seq, int n, int32_t* slots_o
   if (n < 0 || (n > 0 && !slots_out)) return pkv::fail(PKV_ERR_INVALID_ARG, "bad count or NULL slots");
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return pkv::fail(PKV_ERR_INVALID_ARG, "no sequence %d", seq);
+  if (it->second.swapped) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d is swapped out", seq);
   Sequence& s = it->second;
   const int64_t bs = a->block_size;
   if (s.tokens + n > static_cast<int64_t>(INT32_MAX) / 2)
@@ -309,6 +322,7 @@ int pkv_seq_trim_window(pkv_allocator* a, int32_t seq, int window, int32_t* rele
     return pkv::fail(PKV_ERR_INVALID_ARG, "window must be positive and n_released given");
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return pkv::fail(PKV_ERR_INVALID_ARG, "no sequence %d", seq);
+  if (it->second.swapped) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d is swapped out", seq);
   Sequence& s = it->second;
   // Blocks before the one holding token max(0, tokens - window) hold no token
   // of the window.
@@ -331,13 +345,112 @@ int pkv_seq_trim_window(pkv_allocator* a, int32_t seq, int window, int32_t* rele
   PKV_API_END
 }
 
+int pkv_allocator_set_host_pool(pkv_allocator* a, int num_host_blocks) {
+  PKV_API_BEGIN
+  if (int rc = check_alloc(a)) return rc;
+  if (num_host_blocks < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_host_blocks %d is negative", num_host_blocks);
+  for (const auto& kv : a->seqs)
+    if (kv.second.swapped)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d is swapped out", kv.first);
+  a->num_host_blocks = num_host_blocks;
+  a->host_free.resize(num_host_blocks);
+  for (int i = 0; i < num_host_blocks; ++i) a->host_free[i] = i;
+  return PKV_OK;
+  PKV_API_END
+}
+
+int pkv_host_num_free(const pkv_allocator* a, int* out) {
+  PKV_API_BEGIN
+  if (int rc = check_alloc(a)) return rc;
+  if (!out) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL output");
+  *out = static_cast<int>(a->host_free.size());
+  return PKV_OK;
+  PKV_API_END
+}
+
+int pkv_seq_swap_out(pkv_allocator* a, int32_t seq, int32_t* pairs, int cap, int* n_pairs) {
+  PKV_API_BEGIN
+  if (int rc = check_alloc(a)) return rc;
+  if (!n_pairs || (cap > 0 && !pairs)) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL output");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return pkv::fail(PKV_ERR_INVALID_ARG, "no sequence %d", seq);
+  Sequence& s = it->second;
+  if (s.swapped) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d is swapped out", seq);
+  int need = 0;
+  for (int32_t b : s.blocks) need += b >= 0;
+  *n_pairs = need;
+  if (need > static_cast<int>(a->host_free.size()))
+    return pkv::fail(PKV_ERR_OOM, "need %d host blocks, %zu free", need, a->host_free.size());
+  if (cap < need) return pkv::fail(PKV_ERR_INVALID_ARG, "capacity %d < %d pairs", cap, need);
+  int k = 0;
+  for (int32_t& b : s.blocks) {
+    if (b < 0) continue;
+    const int32_t h = a->host_free.back();
+    a->host_free.pop_back();
+    pairs[2 * k] = b;
+    pairs[2 * k + 1] = h;
+    ++k;
+    a->drop_ref(b);  // a block shared with other sequences stays theirs
+    b = h;
+  }
+  s.swapped = true;
+  return PKV_OK;
+  PKV_API_END
+}
+
+int pkv_seq_swap_in(pkv_allocator* a, int32_t seq, int32_t* pairs, int cap, int* n_pairs) {
+  PKV_API_BEGIN
+  if (int rc = check_alloc(a)) return rc;
+  if (!n_pairs || (cap > 0 && !pairs)) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL output");
+  auto it = a->seqs.find(seq);
+  if (it == a->seqs.end()) return pkv::fail(PKV_ERR_INVALID_ARG, "no sequence %d", seq);
+  Sequence& s = it->second;
+  if (!s.swapped) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d is not swapped out", seq);
+  int need = 0;
+  for (int32_t h : s.blocks) need += h >= 0;
+  *n_pairs = need;
+  if (need > static_cast<int>(a->free_list.size()))
+    return pkv::fail(PKV_ERR_OOM, "need %d device blocks, %zu free", need, a->free_list.size());
+  if (cap < need) return pkv::fail(PKV_ERR_INVALID_ARG, "capacity %d < %d pairs", cap, need);
+  int k = 0;
+  for (int32_t& h : s.blocks) {
+    if (h < 0) continue;
+    const int32_t d = a->pop_block();
+    pairs[2 * k] = h;
+    pairs[2 * k + 1] = d;
+    ++k;
+    a->host_free.push_back(h);
+    h = d;
+  }
+  s.swapped = false;
+  return PKV_OK;
+  PKV_API_END
+}
+
+int pkv_seq_is_swapped(const pkv_allocator* a, int32_t seq, int* out) {
+  PKV_API_BEGIN
+  if (int rc = check_alloc(a)) return rc;
+  if (!out) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL output");
+  const Sequence* s;
+  if (int rc = find_seq(a, seq, &s)) return rc;
+  *out = s->swapped ? 1 : 0;
+  return PKV_OK;
+  PKV_API_END
+}
+
 int pkv_seq_free(pkv_allocator* a, int32_t seq) {
   PKV_API_BEGIN
   if (int rc = check_alloc(a)) return rc;
   auto it = a->seqs.find(seq);
   if (it == a->seqs.end()) return pkv::fail(PKV_ERR_INVALID_ARG, "no sequence %d", seq);
-  for (int32_t b : it->second.blocks)
-    if (b >= 0) a->drop_ref(b);
+  for (int32_t b : it->second.blocks) {
+    if (b < 0) continue;
+    if (it->second.swapped)
+      a->host_free.push_back(b);
+    else
+      a->drop_ref(b);
+  }
   a->seqs.erase(it);
   return PKV_OK;
   PKV_API_END
@@ -372,7 +485,7 @@ int pkv_seq_physical_block(const pkv_allocator* a, int32_t seq, int token, int32
   if (int rc = check_alloc(a)) return rc;
   if (!out) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL output");
   const Sequence* s;
-  if (int rc = find_seq(a, seq, &s)) return rc;
+  if (int rc = find_resident(a, seq, &s)) return rc;
   const int64_t idx = token / a->block_size;
   if (token < 0 || idx >= static_cast<int64_t>(s->blocks.size()) || s->blocks[idx] < 0)
     return pkv::fail(PKV_ERR_INDEX, "token %d: logical block %lld is not allocated", token,
@@ -390,7 +503,7 @@ int pkv_export_block_tables(const pkv_allocator* a, const int32_t* seqs, int n, 
     return pkv::fail(PKV_ERR_INVALID_ARG, "bad count or NULL buffer");
   for (int i = 0; i < n; ++i) {
     const Sequence* s;
-    if (int rc = find_seq(a, seqs[i], &s)) return rc;
+    if (int rc = find_resident(a, seqs[i], &s)) return rc;
     if (static_cast<int64_t>(s->blocks.size()) > max_blocks)
       return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d holds %zu blocks > max_blocks %d", seqs[i],
                        s->blocks.size(), max_blocks);

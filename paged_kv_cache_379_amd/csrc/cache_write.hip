@@ -1,5 +1,5 @@
-// The cache write (reshape_and_cache), the block copy behind copy-on-write,
-// and a plain streaming copy used as the bandwidth reference.
+// The cache write (reshape_and_cache), the block copies behind copy-on-write
+// and swapping, and a plain streaming copy used as the bandwidth reference.
 //
 // Page keys:
 //   [P1] "大模型KV Cache内存优化与PagedAttention显存管理机制详解" (yunthe.com)
@@ -89,17 +89,24 @@ hipError_t launch_write(const CacheWriteArgs& a, int num_tokens, hipStream_t s) 
 }
 
 // ---------------------------------------------------------------------------
-// Block copies for copy-on-write: pairs travel by value in the kernel
-// arguments, so no host-to-device transfer is needed.
-constexpr int kPairsPerLaunch = 64;
+// Whole-block copies: copy-on-write (device to device) and swapping (device
+// to pinned host and back, through the host memory's device mapping).  Pairs
+// travel by value in the kernel arguments, so no host-to-device transfer of
+// the pair list is needed.
+constexpr int kPairsPerLaunch = 192;
 constexpr int kCopyThreads = 256;
-constexpr int64_t kCopyChunk = kCopyThreads * 16 * 4;  // bytes per workgroup
+constexpr int kCopyUnroll = 4;
+constexpr int64_t kCopyChunk = kCopyThreads * 16 * kCopyUnroll;  // bytes per workgroup
 
 struct CopyBlocksArgs {
-  uint8_t* key_cache;
-  uint8_t* value_cache;
-  float* k_scales;
-  float* v_scales;
+  const uint8_t* src_k;
+  const uint8_t* src_v;
+  uint8_t* dst_k;
+  uint8_t* dst_v;
+  const float* src_ks;  // scales, NULL for float caches
+  const float* src_vs;
+  float* dst_ks;
+  float* dst_vs;
   int64_t block_bytes;
   int scale_stride;
   int n;
@@ -107,22 +114,81 @@ struct CopyBlocksArgs {
   int32_t dst[kPairsPerLaunch];
 };
 
+// Grid (pair, chunk of the block, K or V).  Every thread issues its loads
+// before its stores, so a workgroup keeps kCopyUnroll 16-byte requests per
+// lane in flight (this matters when the source sits across PCIe).
 __global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(CopyBlocksArgs a) {
   const int p = blockIdx.x;
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kCopyChunk;
   const bool is_v = blockIdx.z != 0;
-  uint8_t* base = is_v ? a.value_cache : a.key_cache;
-  const uint4* s = reinterpret_cast<const uint4*>(base + a.src[p] * a.block_bytes + c0);
-  uint4* d = reinterpret_cast<uint4*>(base + a.dst[p] * a.block_bytes + c0);
+  const uint4* s = reinterpret_cast<const uint4*>((is_v ? a.src_v : a.src_k) +
+                                                  a.src[p] * a.block_bytes + c0);
+  uint4* d = reinterpret_cast<uint4*>((is_v ? a.dst_v : a.dst_k) + a.dst[p] * a.block_bytes + c0);
   int64_t nvec = (a.block_bytes - c0) / 16;
   if (nvec > kCopyChunk / 16) nvec = kCopyChunk / 16;
-  for (int64_t i = threadIdx.x; i < nvec; i += kCopyThreads) d[i] = s[i];
-  float* sc = is_v ? a.v_scales : a.k_scales;
-  if (sc && blockIdx.y == 0) {
-    for (int i = threadIdx.x; i < a.scale_stride; i += kCopyThreads)
-      sc[static_cast<int64_t>(a.dst[p]) * a.scale_stride + i] =
-          sc[static_cast<int64_t>(a.src[p]) * a.scale_stride + i];
+  const int i0 = threadIdx.x;
+  if (nvec == kCopyChunk / 16) {
+    uint4 r[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) r[u] = s[i0 + u * kCopyThreads];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) d[i0 + u * kCopyThreads] = r[u];
+  } else {
+    for (int64_t i = i0; i < nvec; i += kCopyThreads) d[i] = s[i];
   }
+  const float* ss = is_v ? a.src_vs : a.src_ks;
+  float* ds = is_v ? a.dst_vs : a.dst_ks;
+  if (ss && blockIdx.y == 0) {
+    for (int i = threadIdx.x; i < a.scale_stride; i += kCopyThreads)
+      ds[static_cast<int64_t>(a.dst[p]) * a.scale_stride + i] =
+          ss[static_cast<int64_t>(a.src[p]) * a.scale_stride + i];
+  }
+}
+
+// Checks shared by the block copies: ids in range, destinations distinct.
+int check_pairs(const int32_t* pairs, int n_pairs, int num_src, int num_dst,
+                std::vector<char>* is_dst_out) {
+  std::vector<char> is_dst(num_dst, 0);
+  for (int i = 0; i < n_pairs; ++i) {
+    const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= num_src || d < 0 || d >= num_dst)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "pair %d (%d, %d) outside [0, %d) x [0, %d)", i, s, d,
+                       num_src, num_dst);
+    if (is_dst[d]) return pkv::fail(PKV_ERR_INVALID_ARG, "block %d is a destination twice", d);
+    is_dst[d] = 1;
+  }
+  if (is_dst_out) is_dst_out->swap(is_dst);
+  return PKV_OK;
+}
+
+int launch_block_copies(CopyBlocksArgs a, const int32_t* pairs, int n_pairs, hipStream_t st) {
+  const int64_t chunks = (a.block_bytes + kCopyChunk - 1) / kCopyChunk;
+  if (chunks > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "block_bytes too large");
+  for (int base = 0; base < n_pairs; base += kPairsPerLaunch) {
+    a.n = n_pairs - base < kPairsPerLaunch ? n_pairs - base : kPairsPerLaunch;
+    for (int i = 0; i < a.n; ++i) {
+      a.src[i] = pairs[2 * (base + i)];
+      a.dst[i] = pairs[2 * (base + i) + 1];
+    }
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.n, static_cast<unsigned>(chunks), 2),
+                       dim3(kCopyThreads), 0, st, a);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return pkv::fail(PKV_ERR_HIP, "copy launch: %s", hipGetErrorString(err));
+  }
+  return PKV_OK;
+}
+
+// Device address of pinned host memory (NULL stays NULL).
+int host_mapping(void* host, const char* what, void** dev) {
+  *dev = nullptr;
+  if (!host) return PKV_OK;
+  const hipError_t err = hipHostGetDevicePointer(dev, host, 0);
+  if (err != hipSuccess || !*dev) {
+    (void)hipGetLastError();  // clear the sticky error left by the failed query
+    return pkv::fail(PKV_ERR_INVALID_ARG, "%s is not pinned host memory (hipHostMalloc): %s", what,
+                     hipGetErrorString(err));
+  }
+  return PKV_OK;
 }
 
 // ---------------------------------------------------------------------------
@@ -211,40 +277,69 @@ int pkv_copy_blocks(void* key_cache, void* value_cache, float* k_scales, float* 
   if (!key_cache || !value_cache || !pairs) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL pointer");
   if ((k_scales != nullptr) != (v_scales != nullptr) || (k_scales && scale_stride <= 0))
     return pkv::fail(PKV_ERR_INVALID_ARG, "scales must be given together with scale_stride > 0");
-  std::vector<char> is_dst(num_blocks, 0), is_src(num_blocks, 0);
-  for (int i = 0; i < n_pairs; ++i) {
-    const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
-    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
-      return pkv::fail(PKV_ERR_INVALID_ARG, "pair %d (%d, %d) outside [0, %d)", i, s, d, num_blocks);
-    if (is_dst[d]) return pkv::fail(PKV_ERR_INVALID_ARG, "block %d is a destination twice", d);
-    is_dst[d] = 1;
-    is_src[s] = 1;
-  }
+  std::vector<char> is_dst;
+  if (int rc = check_pairs(pairs, n_pairs, num_blocks, num_blocks, &is_dst)) return rc;
   for (int i = 0; i < n_pairs; ++i)
-    if (is_src[pairs[2 * i + 1]])
-      return pkv::fail(PKV_ERR_INVALID_ARG, "block %d is both source and destination", pairs[2 * i + 1]);
-  const int64_t chunks = (static_cast<int64_t>(block_bytes) + kCopyChunk - 1) / kCopyChunk;
-  if (chunks > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "block_bytes too large");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  for (int base = 0; base < n_pairs; base += kPairsPerLaunch) {
-    CopyBlocksArgs a;
-    a.key_cache = static_cast<uint8_t*>(key_cache);
-    a.value_cache = static_cast<uint8_t*>(value_cache);
-    a.k_scales = k_scales;
-    a.v_scales = v_scales;
-    a.block_bytes = static_cast<int64_t>(block_bytes);
-    a.scale_stride = scale_stride;
-    a.n = n_pairs - base < kPairsPerLaunch ? n_pairs - base : kPairsPerLaunch;
-    for (int i = 0; i < a.n; ++i) {
-      a.src[i] = pairs[2 * (base + i)];
-      a.dst[i] = pairs[2 * (base + i) + 1];
-    }
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.n, static_cast<unsigned>(chunks), 2),
-                       dim3(kCopyThreads), 0, st, a);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return pkv::fail(PKV_ERR_HIP, "copy launch: %s", hipGetErrorString(err));
-  }
-  return PKV_OK;
+    if (is_dst[pairs[2 * i]])
+      return pkv::fail(PKV_ERR_INVALID_ARG, "block %d is both source and destination", pairs[2 * i]);
+  CopyBlocksArgs a;
+  a.src_k = a.dst_k = static_cast<uint8_t*>(key_cache);
+  a.src_v = a.dst_v = static_cast<uint8_t*>(value_cache);
+  a.src_ks = a.dst_ks = k_scales;
+  a.src_vs = a.dst_vs = v_scales;
+  a.block_bytes = static_cast<int64_t>(block_bytes);
+  a.scale_stride = scale_stride;
+  return launch_block_copies(a, pairs, n_pairs, static_cast<hipStream_t>(stream));
+  PKV_API_END
+}
+
+int pkv_swap_blocks(void* key_cache, void* value_cache, float* k_scales, float* v_scales,
+                    void* host_key, void* host_value, float* host_k_scales, float* host_v_scales,
+                    const int32_t* pairs, int n_pairs, size_t block_bytes, int num_blocks,
+                    int num_host_blocks, int scale_stride, int direction, void* stream) {
+  PKV_API_BEGIN
+  if (n_pairs < 0 || num_blocks <= 0 || num_host_blocks <= 0 || block_bytes == 0 ||
+      block_bytes % 16)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "bad count, pool size or block_bytes (%zu, multiple "
+                     "of 16)", block_bytes);
+  if (direction != PKV_SWAP_OUT && direction != PKV_SWAP_IN)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "direction %d is neither PKV_SWAP_OUT nor PKV_SWAP_IN",
+                     direction);
+  if (n_pairs == 0) return PKV_OK;
+  if (!key_cache || !value_cache || !host_key || !host_value || !pairs)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL pointer");
+  if ((k_scales != nullptr) != (v_scales != nullptr) ||
+      (k_scales != nullptr) != (host_k_scales != nullptr) ||
+      (k_scales != nullptr) != (host_v_scales != nullptr) || (k_scales && scale_stride <= 0))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "device and host scales must be given together, "
+                     "with scale_stride > 0");
+  if (reinterpret_cast<uintptr_t>(host_key) % 16 || reinterpret_cast<uintptr_t>(host_value) % 16)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "host pools must be 16-byte aligned");
+  const bool out = direction == PKV_SWAP_OUT;
+  if (int rc = check_pairs(pairs, n_pairs, out ? num_blocks : num_host_blocks,
+                           out ? num_host_blocks : num_blocks, nullptr))
+    return rc;
+  void *hk, *hv, *hks, *hvs;
+  if (int rc = host_mapping(host_key, "host_key", &hk)) return rc;
+  if (int rc = host_mapping(host_value, "host_value", &hv)) return rc;
+  if (int rc = host_mapping(host_k_scales, "host_k_scales", &hks)) return rc;
+  if (int rc = host_mapping(host_v_scales, "host_v_scales", &hvs)) return rc;
+  CopyBlocksArgs a;
+  uint8_t* dk = static_cast<uint8_t*>(key_cache);
+  uint8_t* dv = static_cast<uint8_t*>(value_cache);
+  uint8_t* mk = static_cast<uint8_t*>(hk);
+  uint8_t* mv = static_cast<uint8_t*>(hv);
+  a.src_k = out ? dk : mk;
+  a.src_v = out ? dv : mv;
+  a.dst_k = out ? mk : dk;
+  a.dst_v = out ? mv : dv;
+  a.src_ks = out ? k_scales : static_cast<float*>(hks);
+  a.src_vs = out ? v_scales : static_cast<float*>(hvs);
+  a.dst_ks = out ? static_cast<float*>(hks) : k_scales;
+  a.dst_vs = out ? static_cast<float*>(hvs) : v_scales;
+  a.block_bytes = static_cast<int64_t>(block_bytes);
+  a.scale_stride = scale_stride;
+  return launch_block_copies(a, pairs, n_pairs, static_cast<hipStream_t>(stream));
   PKV_API_END
 }
 

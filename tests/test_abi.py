@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(lib, name), f"{name} declared in pkv.h but not exported"
     # the binding wraps exactly the declared set
     assert sorted(pkv.EXPORTED) == names
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
 
 
 def _header_params():
@@ -164,6 +164,33 @@ def test_cache_write_and_copy_reject_bad_arguments():
     ok = np.array([[1, 2]], np.int32)
     assert c(1, 1, None, None, ok.ctypes.data_as(i32p), 1, 4000 + 8, 8, 2, None) == pkv.ERR_INVALID_ARG
     assert lib.pkv_stream_copy(1, 1, 24, None) == pkv.ERR_INVALID_ARG
+
+
+def test_swap_rejects_bad_arguments():
+    """Checks that run on the host before the pinned pools are looked up."""
+    lib = pkv.load()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    sw = lib.pkv_swap_blocks
+
+    def call(pairs, direction=pkv.SWAP_OUT, nb=8, nhb=4, block_bytes=4096, scales=(None,) * 4,
+             hk=16, stride=2):
+        pairs = np.ascontiguousarray(np.asarray(pairs, np.int32).reshape(-1, 2))
+        return sw(16, 16, scales[0], scales[1], hk, 16, scales[2], scales[3],
+                  pairs.ctypes.data_as(i32p), len(pairs), block_bytes, nb, nhb, stride,
+                  direction, None)
+
+    assert call([[7, 3]], direction=2) == pkv.ERR_INVALID_ARG           # no such direction
+    assert call([[7, 4]]) == pkv.ERR_INVALID_ARG                        # host id 4 of 4
+    assert call([[8, 3]]) == pkv.ERR_INVALID_ARG                        # device id 8 of 8
+    assert call([[4, 7]], direction=pkv.SWAP_IN) == pkv.ERR_INVALID_ARG  # host id 4 of 4
+    assert call([[1, 2], [5, 2]]) == pkv.ERR_INVALID_ARG                # destination twice
+    assert call([[1, 2]], block_bytes=4000) == pkv.ERR_INVALID_ARG      # not a multiple of 16
+    assert call([[1, 2]], hk=None) == pkv.ERR_INVALID_ARG
+    assert call([[1, 2]], hk=24) == pkv.ERR_INVALID_ARG                 # misaligned pool
+    assert call([[1, 2]], scales=(16, 16, None, None)) == pkv.ERR_INVALID_ARG
+    assert call([[1, 2]], scales=(16, 16, 16, 16), stride=0) == pkv.ERR_INVALID_ARG
+    assert call([[1, 2]], nhb=0) == pkv.ERR_INVALID_ARG
+    assert call(np.zeros((0, 2))) == pkv.OK                            # nothing to copy
 
 
 def test_validate_tables():

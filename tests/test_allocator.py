@@ -94,9 +94,12 @@ def test_differential_against_model(seed):
     order = rng.permutation(nb).tolist()
     model.set_free_order(order)
     lib.set_free_order(order)
+    nhb = int(rng.integers(0, nb))
+    model.set_host_pool(nhb)
+    lib.set_host_pool(nhb)
     live = []
     for step in range(1500):
-        r = rng.integers(0, 10)
+        r = rng.integers(0, 12)
         if r == 0 or not live:
             a, b = _apply(model, "seq_create", ()), _apply(lib, "seq_create", ())
             assert a == b
@@ -110,7 +113,8 @@ def test_differential_against_model(seed):
             sid = live[rng.integers(len(live))]
             a, b = _apply(model, "seq_fork", (sid,)), _apply(lib, "seq_fork", (sid,))
             assert a == b
-            live.append(a[1])
+            if a[0] == "ok":
+                live.append(a[1])
         elif r == 6:
             sid = live.pop(rng.integers(len(live)))
             assert _apply(model, "seq_free", (sid,)) == _apply(lib, "seq_free", (sid,))
@@ -120,7 +124,8 @@ def test_differential_against_model(seed):
             op = ["free", "incref"][int(rng.integers(2))]
             if op == "free":
                 # never free blocks a live sequence still owns through its table
-                owned = {b for s in live for b in model.seqs[s]["blocks"] if b >= 0}
+                owned = {b for s in live for b in model.seqs[s]["blocks"]
+                         if b >= 0 and not model.seqs[s]["swapped"]}
                 ids = [i for i in ids if i not in owned] or [nb + 5]
             a, b = _apply(model, op, (ids,)), _apply(lib, op, (ids,))
             assert a[0] == b[0], (step, op, ids, a, b)
@@ -137,14 +142,25 @@ def test_differential_against_model(seed):
             tok = int(rng.integers(-2, 4 * bs))
             assert _apply(model, "seq_physical_block", (sid, tok)) == \
                 _apply(lib, "seq_physical_block", (sid, tok))
-        else:
+        elif r == 9:
             mb = int(rng.integers(0, 8))
-            a = _apply(model, "export_block_tables", (live, mb, -1))
-            b = _apply(lib, "export_block_tables", (live, mb, -1))
+            # usually the resident sequences; sometimes all (a swapped one is an error)
+            sel = live if rng.integers(4) == 0 else [s for s in live if not model.seq_is_swapped(s)]
+            a = _apply(model, "export_block_tables", (sel, mb, -1))
+            b = _apply(lib, "export_block_tables", (sel, mb, -1))
             assert a[0] == b[0]
             if a[0] == "ok":
-                assert np.array_equal(np.array(a[1][0]).reshape(len(live), mb), b[1][0])
+                assert np.array_equal(np.array(a[1][0]).reshape(len(sel), mb), b[1][0])
                 assert list(a[1][1]) == b[1][1].tolist()
+        else:
+            sid = live[rng.integers(len(live))]
+            op = "seq_swap_out" if r == 10 else "seq_swap_in"
+            a, b = _apply(model, op, (sid,)), _apply(lib, op, (sid,))
+            assert a == b, (step, op, a, b)
+        for sid in live:
+            assert model.seqs[sid]["blocks"] == lib.seq_block_ids(sid)
+            assert model.seq_is_swapped(sid) == lib.seq_is_swapped(sid)
+        assert len(model.host_free) == lib.host_num_free()
         assert model.ref_count == [lib.ref_count(i) for i in range(nb)]
         assert model.free_blocks == lib.free_list()
         assert model.usage_ratio() == pytest.approx(lib.usage_ratio())
@@ -214,3 +230,67 @@ def test_trim_window_keeps_cache_constant():
         a.seq_trim_window(sid, 0)
     a.seq_free(sid)
     assert a.num_free() == 8
+
+
+def test_swap_out_and_in_round_trip():
+    """[P1] scheduler section, preemption: swapping a sequence out frees the
+    device blocks it alone held (shared prefix blocks stay with the other
+    sequences), the sequence is frozen while out, and swapping in gives it
+    fresh device blocks with the same token count."""
+    bs = 4
+    a = pkv.BlockAllocator(12, bs)
+    a.set_host_pool(6)
+    p = a.seq_create()
+    a.seq_append_tokens(p, 8)            # 2 full prompt blocks
+    c = a.seq_fork(p)                    # shares both
+    a.seq_append_tokens(c, 3)            # + 1 own block
+    shared = a.seq_block_ids(p)
+    own = a.seq_block_ids(c)[2]
+    free0 = a.num_free()
+    pairs = a.seq_swap_out(c)
+    assert [d for d, _ in pairs] == a.seq_block_ids(p) + [own]
+    assert [h for _, h in pairs] == [5, 4, 3]  # host blocks leave from the end
+    assert a.seq_is_swapped(c) and a.host_num_free() == 3
+    assert a.num_free() == free0 + 1      # only the block c alone held
+    assert [a.ref_count(b) for b in shared] == [1, 1] and a.ref_count(own) == 0
+    assert a.seq_block_ids(c) == [5, 4, 3] and a.seq_num_tokens(c) == 11
+    for op, args in (("seq_append_tokens", (c, 1)), ("seq_fork", (c,)),
+                     ("seq_trim_window", (c, 4)), ("seq_physical_block", (c, 0)),
+                     ("export_block_tables", ([c], 4)), ("seq_swap_out", (c,))):
+        with pytest.raises(ValueError):
+            getattr(a, op)(*args)
+    with pytest.raises(ValueError):
+        a.seq_swap_in(p)                  # not swapped out
+    with pytest.raises(ValueError):
+        a.set_host_pool(8)                # a sequence is out
+    back = a.seq_swap_in(c)
+    assert [h for h, _ in back] == [5, 4, 3] and a.host_num_free() == 6
+    new = a.seq_block_ids(c)
+    assert [d for _, d in back] == new and not set(new) & set(shared)
+    assert all(a.ref_count(b) == 1 for b in new + shared)
+    a.seq_append_tokens(c, 1)             # resumes where it stopped
+    assert a.seq_num_tokens(c) == 12
+    a.seq_free(c)
+    a.seq_free(p)
+    assert a.num_free() == 12
+
+
+def test_swap_is_all_or_nothing():
+    bs = 4
+    a = pkv.BlockAllocator(6, bs)
+    a.set_host_pool(2)
+    s = a.seq_create()
+    a.seq_append_tokens(s, 12)            # 3 blocks > 2 host blocks
+    ids = a.seq_block_ids(s)
+    with pytest.raises(pkv.OutOfBlocks):
+        a.seq_swap_out(s)
+    assert a.seq_block_ids(s) == ids and not a.seq_is_swapped(s) and a.host_num_free() == 2
+    a.set_host_pool(3)
+    a.seq_swap_out(s)
+    t = a.seq_create()
+    a.seq_append_tokens(t, 16)            # takes 4 of the 6 device blocks
+    with pytest.raises(pkv.OutOfBlocks):
+        a.seq_swap_in(s)                  # needs 3, 2 free
+    assert a.seq_is_swapped(s) and a.host_num_free() == 0 and a.num_free() == 2
+    a.seq_free(s)                         # a swapped-out sequence frees host blocks
+    assert a.host_num_free() == 3 and a.num_free() == 2

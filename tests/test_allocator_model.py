@@ -143,3 +143,153 @@ def test_random_ops_invariants():
         a.seq_free(sid)
     assert not any(a.ref_count)
     assert sorted(a.free_blocks) == list(range(64))
+
+
+# ---------------------------------------------------------------------------
+# Swap pool ([P1] scheduler section, item 3: a preempted request's KV goes to
+# CPU memory, its device blocks are freed, and it is copied back later).  The
+# pins below simulate the memory contents the pair lists move, so they check
+# the model against what a swap must achieve, not against its own code.
+
+def _write_tokens(mem, slots, bs, values):
+    for slot, v in zip(slots, values):
+        mem.setdefault(slot // bs, {})[slot % bs] = v
+
+
+def _gather(model, sid, mem):
+    seq = model.seqs[sid]
+    bs = model.block_size
+    return [mem[seq["blocks"][t // bs]][t % bs] for t in range(seq["tokens"])]
+
+
+def pin_swap_round_trip_preserves_contents(cls):
+    """Contents survive swap-out, reuse of the freed device blocks by another
+    request, and swap-in to different blocks; the running sequence that
+    shares the preempted one's prompt blocks is never disturbed."""
+    bs = 4
+    m = cls(16, bs)
+    m.set_host_pool(8)
+    dev, host = {}, {}
+    p = m.seq_create()
+    slots, _ = m.seq_append_tokens(p, 10)
+    _write_tokens(dev, slots, bs, [("p", i) for i in range(10)])
+    c = m.seq_fork(p)
+    slots, cow = m.seq_append_tokens(c, 7)
+    for s_, d_ in cow:
+        dev[d_] = dict(dev[s_])
+    _write_tokens(dev, slots, bs, [("c", i) for i in range(7)])
+    want_c, want_p = _gather(m, c, dev), _gather(m, p, dev)
+    for d_, h_ in m.seq_swap_out(c):
+        host[h_] = dict(dev[d_])
+    assert m.seq_is_swapped(c)
+    n = m.seq_create()                      # another request takes the freed blocks
+    slots, _ = m.seq_append_tokens(n, len(m.free_blocks) * bs)
+    _write_tokens(dev, slots, bs, ["junk"] * len(slots))
+    assert _gather(m, p, dev) == want_p
+    m.seq_free(n)
+    for h_, d_ in m.seq_swap_in(c):
+        dev[d_] = dict(host[h_])
+    assert not m.seq_is_swapped(c)
+    assert _gather(m, c, dev) == want_c and _gather(m, p, dev) == want_p
+    # it resumes: the next token lands after the restored ones
+    slots, cow = m.seq_append_tokens(c, 1)
+    assert not cow and slots[0] // bs == m.seqs[c]["blocks"][-1]
+
+
+def pin_swap_conservation(cls):
+    """Random operations with swaps: every device block is either free or
+    held by resident sequences exactly as often as its count says; every host
+    block is either free or held by exactly one swapped-out sequence; swapping
+    every sequence out frees the whole device pool."""
+    rng = np.random.default_rng(9)
+    nb, nhb, bs = 24, 20, 4
+    m = cls(nb, bs)
+    m.set_host_pool(nhb)
+    live = []
+    for _ in range(1500):
+        op = int(rng.integers(0, 6))
+        try:
+            if op == 0 or not live:
+                live.append(m.seq_create())
+            elif op == 1:
+                m.seq_append_tokens(live[rng.integers(len(live))], int(rng.integers(1, 9)))
+            elif op == 2:
+                live.append(m.seq_fork(live[rng.integers(len(live))]))
+            elif op == 3:
+                m.seq_free(live.pop(rng.integers(len(live))))
+            elif op == 4:
+                m.seq_swap_out(live[rng.integers(len(live))])
+            else:
+                m.seq_swap_in(live[rng.integers(len(live))])
+        except (OutOfBlocks, ValueError):
+            pass
+        refs = np.zeros(nb, int)
+        held_host = []
+        for sid in live:
+            ids = [b for b in m.seqs[sid]["blocks"] if b >= 0]
+            if m.seq_is_swapped(sid):
+                held_host += ids
+            else:
+                np.add.at(refs, ids, 1)
+        assert refs.tolist() == m.ref_count
+        assert sorted(m.free_blocks + [b for b in range(nb) if refs[b]]) == list(range(nb))
+        assert sorted(m.host_free + held_host) == list(range(nhb))
+    for sid in [s for s in live if m.seq_is_swapped(s)]:
+        m.seq_free(sid)
+        live.remove(sid)
+    assert sorted(m.host_free) == list(range(nhb))
+    m.set_host_pool(nb * 2)
+    for sid in live:
+        m.seq_swap_out(sid)
+    assert not any(m.ref_count) and sorted(m.free_blocks) == list(range(nb))
+
+
+def pin_swap_all_or_nothing(cls):
+    m = cls(6, 4)
+    m.set_host_pool(2)
+    s = m.seq_create()
+    m.seq_append_tokens(s, 12)
+    before = (list(m.seqs[s]["blocks"]), list(m.free_blocks), list(m.host_free))
+    with pytest.raises(OutOfBlocks):
+        m.seq_swap_out(s)
+    assert (m.seqs[s]["blocks"], m.free_blocks, m.host_free) == before
+    with pytest.raises(ValueError):
+        m.seq_swap_in(s)
+
+
+SWAP_PINS = [pin_swap_round_trip_preserves_contents, pin_swap_conservation, pin_swap_all_or_nothing]
+
+
+@pytest.mark.parametrize("pin", SWAP_PINS, ids=lambda f: f.__name__)
+def test_swap_pins(pin):
+    pin(AllocatorModel)
+
+
+SWAP_MUTATIONS = {
+    "pairs_reversed": ("pairs.append((b, h))", "pairs.append((h, b))"),
+    "out_keeps_reference": ("            self.free([b])\n            seq[\"blocks\"][j] = h",
+                            "            seq[\"blocks\"][j] = h"),
+    "in_keeps_host_block": ("            self.host_free.append(h)\n", ""),
+    "in_pairs_reversed": ("pairs.append((h, d))", "pairs.append((d, h))"),
+    "out_not_all_or_nothing": ("        if len(held) > len(self.host_free):\n            raise OutOfBlocks(f\"need {len(held)} host blocks, {len(self.host_free)} free\")\n",
+                               ""),
+    "in_table_not_updated": ("            seq[\"blocks\"][j] = d\n", ""),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SWAP_MUTATIONS))
+def test_swap_pins_catch_mutation(name):
+    import types
+    import oracle.allocator_model as am
+    old, new = SWAP_MUTATIONS[name]
+    src = open(am.__file__, encoding="utf-8").read()
+    assert src.count(old) == 1, name
+    mod = types.ModuleType(f"allocator_mutant_{name}")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    caught = []
+    for pin in SWAP_PINS:
+        try:
+            pin(mod.AllocatorModel)
+        except (Exception, pytest.fail.Exception):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught {name}"
