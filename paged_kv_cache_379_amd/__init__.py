@@ -100,6 +100,14 @@ def load(path=None):
     if not os.path.exists(path):
         raise RuntimeError(f"libpkv.so not found at {path}: run "
                            "`python -m paged_kv_cache_379_amd.build` first")
+    # torch carries its own HIP runtime.  The library must resolve to that
+    # same runtime (streams and pinned allocations come from torch), so torch
+    # is loaded first; loaded the other way round, the process ends up with
+    # two runtimes and torch's pinned memory is unknown to the library's.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)

