@@ -32,6 +32,8 @@ Readings of points the pages leave open (each also listed in the design doc):
   read, whatever their contents;
 * the int8 cache write rounds ``x / scale`` in fp32, half to even, and
   saturates to [-127, 127];
+* the page's FP8 option is read as OCP E4M3 codes with the same per-(block,
+  kv head) scale, value = decode(code) * scale (``fp8_e4m3``);
 * a sliding window W keeps the last W tokens, the decoded token included:
   positions max(0, n - W) .. n - 1 ([P2] sliding window section).
 
@@ -47,7 +49,10 @@ this file and checks that the pins catch each one.
 """
 import numpy as np
 
-FORMATS = ("f32", "f16", "bf16", "i8")
+from . import fp8_e4m3
+
+FORMATS = ("f32", "f16", "bf16", "i8", "fp8")
+SCALED_FORMATS = ("i8", "fp8")
 
 
 def to_f64(x, fmt):
@@ -66,6 +71,8 @@ def to_f64(x, fmt):
         return np.asarray(x, dtype=np.float16).astype(np.float64)
     if fmt == "i8":
         return np.asarray(x, dtype=np.int8).astype(np.float64)
+    if fmt == "fp8":
+        return fp8_e4m3.decode(x)
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -90,7 +97,7 @@ def gather_context(key_cache, value_cache, table_row, n, block_size, kv_fmt,
         raise IndexError("block table entry outside the physical pool")
     k = to_f64(key_cache[phys, offset], kv_fmt)
     v = to_f64(value_cache[phys, offset], kv_fmt)
-    if kv_fmt == "i8":
+    if kv_fmt in SCALED_FORMATS:
         # One scale per (physical block, kv head), applied to every element of
         # that block's rows for that head.
         k = k * np.asarray(k_scales, dtype=np.float64)[phys][:, :, None]
@@ -106,7 +113,7 @@ def paged_decode(q, q_fmt, key_cache, value_cache, kv_fmt, block_tables,
     q            [B, H, D] in ``q_fmt``
     key_cache    [NB, block_size, Hkv, D] in ``kv_fmt``; value_cache likewise
     block_tables [B, MB] int, context_lens [B] int
-    k_scales, v_scales [NB, Hkv] fp32 (``kv_fmt == "i8"`` only)
+    k_scales, v_scales [NB, Hkv] fp32 (``kv_fmt`` "i8" or "fp8" only)
     window       0, or the sliding window W: only the last W tokens of each
                  context are attended to ([P2] "Sliding Window Attention控制
                  长序列显存": only the most recent W tokens' KV is kept)
@@ -154,7 +161,9 @@ def reshape_and_cache(k, v, src_fmt, key_cache, value_cache, kv_fmt,
     unchanged (``src_fmt`` must equal ``kv_fmt``).  An int8 cache stores
     clip(rint(x / scale), -127, 127) with the existing scale of that
     (block, kv head); the division and the rounding are done in fp32, half to
-    even.  Returns the (possibly copied) caches.
+    even.  An fp8 cache stores the E4M3 code of x / scale (division in fp32,
+    nearest value, ties to even, saturating at 448; see ``fp8_e4m3``).
+    Returns the (possibly copied) caches.
     """
     if not in_place:
         key_cache = key_cache.copy()
@@ -172,6 +181,12 @@ def reshape_and_cache(k, v, src_fmt, key_cache, value_cache, kv_fmt,
                 sc = np.asarray(scales, dtype=np.float32)[blk][:, None]
                 code = np.clip(np.rint(x / sc), -127, 127)
                 cache[blk, off] = code.astype(np.int8)
+        elif kv_fmt == "fp8":
+            for src, cache, scales in ((k, key_cache, k_scales),
+                                       (v, value_cache, v_scales)):
+                x = to_f64(src[t], src_fmt).astype(np.float32)  # exact
+                sc = np.asarray(scales, dtype=np.float32)[blk][:, None]
+                cache[blk, off] = fp8_e4m3.encode(x / sc)
         else:
             if src_fmt != kv_fmt:
                 raise ValueError("float caches take rows of their own format")

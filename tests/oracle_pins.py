@@ -226,6 +226,36 @@ def pin_int8_dequant(pa):
     np.testing.assert_allclose(got[0], want, rtol=0, atol=1e-12)
 
 
+def pin_fp8_dequant(pa):
+    """fp8 (E4M3) codes with per-(block, kv head) scales == SDPA on the values
+    torch's float8_e4m3fn gives the same bytes, times the scale."""
+    rng = np.random.default_rng(22)
+    h, hkv, d = 4, 2, 16
+    g = h // hkv
+    nb = 6
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    kc = rng.choice(finite, size=(nb, BS, hkv, d))
+    vc = rng.choice(finite, size=(nb, BS, hkv, d))
+    ks = rng.uniform(0.001, 0.01, size=(nb, hkv)).astype(np.float32)
+    vs = rng.uniform(0.001, 0.01, size=(nb, hkv)).astype(np.float32)
+    q = rng.standard_normal((1, h, d)).astype(np.float16)
+    tables = np.array([[4, 1, 2]], dtype=np.int32)
+    n = 41
+    got = pa.paged_decode(q, "f16", kc, vc, "fp8", tables, [n], BS, 0.25, ks, vs)
+
+    def tval(codes):
+        return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    k_rows, v_rows = [], []
+    for i in range(n):
+        b, o = tables[0, i // BS], i % BS
+        k_rows.append(tval(kc[b, o]) * ks[b].astype(np.float64)[:, None])
+        v_rows.append(tval(vc[b, o]) * vs[b].astype(np.float64)[:, None])
+    k = np.repeat(np.stack(k_rows), g, axis=1)
+    v = np.repeat(np.stack(v_rows), g, axis=1)
+    want = _sdpa(q[0].astype(np.float64), k, v, 0.25)
+    np.testing.assert_allclose(got[0], want, rtol=0, atol=1e-12)
+
+
 def pin_bf16_decode(pa):
     """bf16 bit patterns decode to the values torch's bfloat16 gives them."""
     rng = np.random.default_rng(19)
@@ -352,10 +382,35 @@ def pin_window_one_and_released_blocks(pa):
     assert np.array_equal(trimmed, full)
 
 
+def pin_cache_write_fp8(pa):
+    """fp8 cache write: per element, torch's float8_e4m3fn rounding of the
+    fp32 quotient clipped to +/-448 (the saturating reading), with the
+    (block, kv head) scale."""
+    rng = np.random.default_rng(23)
+    nb, hkv, d = 4, 2, 8
+    kc = np.zeros((nb, BS, hkv, d), dtype=np.uint8)
+    vc = np.zeros((nb, BS, hkv, d), dtype=np.uint8)
+    ks = np.array([[1.0, 0.5], [0.25, 2.0], [1.0, 1.0], [0.01, 0.02]], dtype=np.float32)
+    vs = ks[::-1].copy()
+    k = (30 * rng.standard_normal((3, hkv, d))).astype(np.float16)
+    v = (30 * rng.standard_normal((3, hkv, d))).astype(np.float16)
+    # a tie (1.0625 lies halfway between 1.0 and 1.125), saturation, a subnormal
+    k[0, 0, :5] = [1.0625, -1.0625, 600.0, -600.0, 2.0 ** -10 * 3]
+    slots = np.array([0 * BS + 1, 1 * BS + 15, 3 * BS + 7], dtype=np.int32)
+    kw, vw = pa.reshape_and_cache(k, v, "f16", kc, vc, "fp8", slots, BS, ks, vs)
+    for t, slot in enumerate(slots):
+        b, o = divmod(int(slot), BS)
+        for src, dst, sc in ((k, kw, ks), (v, vw, vs)):
+            qf = np.clip(src[t].astype(np.float32) / sc[b][:, None], -448, 448)
+            want = torch.from_numpy(qf).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            np.testing.assert_array_equal(dst[b, o], want)
+    assert list(kw[0, 1, 0, :5]) == [0x38, 0xB8, 0x7E, 0xFE, 0x02]
+
+
 ALL_DECODE_PINS = [
     pin_sdpa_contiguous, pin_closed_forms, pin_one_hot, pin_permutation_invariance,
     pin_shared_equals_duplicated, pin_gqa_equals_repeated_mha, pin_unread_slots_ignored,
-    pin_int8_dequant, pin_bf16_decode, pin_window_equals_contiguous_tail,
+    pin_int8_dequant, pin_fp8_dequant, pin_bf16_decode, pin_window_equals_contiguous_tail,
     pin_window_one_and_released_blocks,
 ]
-ALL_CACHE_WRITE_PINS = [pin_cache_write_float, pin_cache_write_int8]
+ALL_CACHE_WRITE_PINS = [pin_cache_write_float, pin_cache_write_int8, pin_cache_write_fp8]

@@ -26,6 +26,8 @@ MUTATIONS = {
     "int8_round_floor": ("code = np.clip(np.rint(x / sc), -127, 127)", "code = np.clip(np.floor(x / sc), -127, 127)"),
     "int8_no_saturation": ("code = np.clip(np.rint(x / sc), -127, 127)", "code = np.rint(x / sc)"),
     "cache_write_ignores_skip": ("        if slot < 0:\n            continue\n", ""),
+    "fp8_scale_dropped": ('    if kv_fmt in SCALED_FORMATS:\n', '    if kv_fmt == "i8":\n'),
+    "fp8_write_no_scale": ("                cache[blk, off] = fp8_e4m3.encode(x / sc)", "                cache[blk, off] = fp8_e4m3.encode(x)"),
 }
 
 
@@ -34,6 +36,7 @@ def _mutant(name):
     src = open(pa.__file__, encoding="utf-8").read()
     assert src.count(old) == 1, f"mutation {name}: pattern must occur exactly once"
     mod = types.ModuleType(f"oracle_mutant_{name}")
+    mod.__package__ = "oracle"   # the oracle's own relative imports resolve
     exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
     return mod
 
