@@ -35,9 +35,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode attention: context tokens attended/s and achieved HBM GB/s (% of peak)"
 HBM_PEAK_GBPS = 8000.0
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "fp8": 1}
+SCALED = ("i8", "fp8")
+TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-3, "i8": 2e-2, "fp8": 2e-3}
 KERNEL_SOURCES = ["decode_kernel.h", "decode_dispatch.h", "decode.hip", "decode_f32.hip",
-                  "decode_f16.hip", "decode_bf16.hip", "decode_i8.hip"]
+                  "decode_f16.hip", "decode_bf16.hip", "decode_i8.hip", "decode_fp8.hip"]
 
 
 def kernel_hash():
@@ -69,7 +71,7 @@ def algorithmic_bytes(wl):
     valid = {b: len(o) for b, o in slots.items()}
     unique_tokens = sum(valid.values())
     kv = 2 * unique_tokens * row
-    scales = 2 * 4 * wl.num_kv_heads * len(valid) if wl.kv_fmt == "i8" else 0
+    scales = 2 * 4 * wl.num_kv_heads * len(valid) if wl.kv_fmt in SCALED else 0
     qo = 2 * wl.num_seqs * wl.num_heads * wl.head_dim * ELEM_BYTES[wl.q_fmt]
     meta = 4 * table_entries + 4 * wl.num_seqs
     return dict(total=kv + scales + qo + meta, kv=kv, unique_tokens=unique_tokens,
@@ -261,7 +263,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3,
-                    help="workload 1..6 (default 3: 70B-shaped fp16; 6: sliding window)")
+                    help="workload 1..8 (default 3: 70B-shaped fp16; 6: sliding window; "
+                         "7, 8: configurations 3 and 5 with an FP8 cache)")
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = library default)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
@@ -304,6 +307,8 @@ def main():
         arr = np.ascontiguousarray(arr)
         if fmt == "bf16":
             return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+        if fmt == "fp8":
+            return torch.from_numpy(arr.view(np.uint8)).to(dev).view(torch.float8_e4m3fn)
         return torch.from_numpy(arr).to(dev)
 
     q = up(wl.q, wl.q_fmt)
@@ -311,8 +316,8 @@ def main():
     tables, lens = up(wl.block_tables, "i32"), up(wl.context_lens, "i32")
     k_new, v_new = up(wl.k_new, wl.new_fmt), up(wl.v_new, wl.new_fmt)
     slots = up(wl.slot_mapping, "i32")
-    ks = up(wl.k_scales, "f32") if wl.kv_fmt == "i8" else None
-    vs = up(wl.v_scales, "f32") if wl.kv_fmt == "i8" else None
+    ks = up(wl.k_scales, "f32") if wl.kv_fmt in SCALED else None
+    vs = up(wl.v_scales, "f32") if wl.kv_fmt in SCALED else None
     out = torch.empty_like(q)
     B, H, D = q.shape
     MB = tables.shape[1]
@@ -418,7 +423,7 @@ def main():
                              wl.kv_fmt, wl.slot_mapping, wl.block_size, wl.k_scales, wl.v_scales,
                              in_place=True)
         err, seqs = parity_sample(wl, out)
-        tol = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-3, "i8": 2e-2}[wl.kv_fmt]
+        tol = TOL[wl.kv_fmt]
         result["parity"] = {"max_abs_err": err, "tol": tol, "seqs": seqs, "ok": err <= tol}
         log(f"parity on seqs {seqs}: max abs err {err:.3g} (tol {tol:g})")
         # the oracle leg below reads the caches as written (idempotent rewrite)

@@ -29,7 +29,8 @@
  *   q, out                  [num_seqs][num_heads][head_dim]
  *   block_tables            int32 [num_seqs][max_blocks_per_seq]
  *   context_lens            int32 [num_seqs]
- *   k_scales, v_scales      fp32 [num_blocks][num_kv_heads]   (int8 caches)
+ *   k_scales, v_scales      fp32 [num_blocks][num_kv_heads]   (int8 and fp8 caches)
+ *                           value of a stored code = decode(code) * scale
  */
 #ifndef PKV_H_
 #define PKV_H_
@@ -53,8 +54,11 @@ enum {
   PKV_ERR_WORKSPACE = 7     /* decode: workspace missing or too small         */
 };
 
-/* Storage formats. */
-enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3 };
+/* Storage formats.  PKV_FP8 is the OCP FP8 E4M3 format (sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; no infinities, 0x7F / 0xFF are NaN, largest
+ * finite 448): the [P2] "量化压缩KV Cache的INT8与FP8方案" FP8 cache option,
+ * whose printed "E4M1" is read as E4M3. */
+enum { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_I8 = 3, PKV_FP8 = 4 };
 
 /* Message describing the calling thread's last failure ("" if none). */
 const char* pkv_last_error(void);

@@ -17,14 +17,14 @@ __all__ = [
     "load", "LIB_PATH", "PkvError", "OutOfBlocks", "DoubleFree",
     "paged_attention_decode", "decode_workspace_size", "decode_partition_size",
     "reshape_and_cache", "copy_blocks", "swap_blocks", "stream_copy", "validate_tables",
-    "BlockAllocator", "F32", "F16", "BF16", "I8", "SWAP_OUT", "SWAP_IN",
+    "BlockAllocator", "F32", "F16", "BF16", "I8", "FP8", "SWAP_OUT", "SWAP_IN",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
 # Status codes and formats (include/pkv.h).
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_OOM, ERR_DOUBLE_FREE, ERR_INDEX, ERR_HIP, ERR_WORKSPACE = range(8)
-F32, F16, BF16, I8 = 0, 1, 2, 3
+F32, F16, BF16, I8, FP8 = 0, 1, 2, 3, 4
 SWAP_OUT, SWAP_IN = 0, 1
 
 
@@ -142,7 +142,8 @@ def _torch():
 
 def _fmt(t):
     torch = _torch()
-    return {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8}[t.dtype]
+    return {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+            torch.float8_e4m3fn: FP8}[t.dtype]
 
 
 def _dev_ptr(t, name, dtype=None):
@@ -185,7 +186,8 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
 
     out, q [B, H, D]; key_cache, value_cache [NB, block_size, Hkv, D];
     block_tables int32 [B, MB]; context_lens int32 [B]; k/v_scales fp32
-    [NB, Hkv] for int8 caches; window: 0 or a sliding window in tokens.  A
+    [NB, Hkv] for int8 and fp8 (torch.float8_e4m3fn) caches; window: 0 or a
+    sliding window in tokens.  A
     workspace of the needed size is allocated from torch when none is given.
     """
     torch = _torch()

@@ -36,6 +36,7 @@ SOURCES = [
     "decode_f16.hip",
     "decode_bf16.hip",
     "decode_i8.hip",
+    "decode_fp8.hip",
     "cache_write.hip",
 ]
 

@@ -41,6 +41,34 @@ struct CacheWriteArgs {
 
 constexpr int kWriteThreads = 256;
 
+// fp32 -> OCP FP8 E4M3 code: the nearest representable value, ties to the
+// even mantissa; magnitudes of 448 and above (infinities included) saturate
+// to 448 and NaN gives 0x7F.  Below 2^-6 the values are the multiples of
+// 2^-9 (subnormals); above, 8 steps per binade: q = a * 2^(3 - e) lies in
+// [8, 16], and q = 16 carries into the next exponent by itself.
+__device__ __forceinline__ uint32_t encode_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.f) return sign | 0x7Eu;
+  if (a < 0.015625f) return sign | static_cast<uint32_t>(rintf(a * 512.f));
+  const int e = static_cast<int>((__float_as_uint(a) >> 23) & 0xFFu) - 127;
+  const uint32_t q = static_cast<uint32_t>(rintf(ldexpf(a, 3 - e)));
+  return sign | ((static_cast<uint32_t>(e + 7) << 3) + q - 8u);
+}
+
+// The stored byte of x / scale for a one-byte cache format (IEEE division).
+template <int KF>
+__device__ __forceinline__ uint32_t quantise_byte(float x, float sc) {
+  if constexpr (KF == PKV_I8) {
+    float qv = rintf(x / sc);  // round half to even
+    qv = fminf(fmaxf(qv, -127.f), 127.f);
+    return static_cast<uint32_t>(static_cast<int32_t>(qv)) & 0xFFu;
+  } else {
+    return encode_e4m3(x / sc);
+  }
+}
+
 template <int SF, int KF>
 __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(CacheWriteArgs a) {
   const int t = blockIdx.x;
@@ -50,7 +78,7 @@ __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(CacheWriteAr
   const uint8_t* src = is_v ? a.v : a.k;
   uint8_t* dst = is_v ? a.value_cache : a.key_cache;
   const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * a.head_dim;
-  if constexpr (KF != PKV_I8) {
+  if constexpr (!pkv_dev::scaled_format(KF)) {
     static_assert(SF == KF, "float caches take rows of their own format");
     const int64_t vecs = row_elems * Format<KF>::kBytes / 16;
     const uint4* s4 = reinterpret_cast<const uint4*>(src) + t * vecs;
@@ -71,12 +99,7 @@ __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(CacheWriteAr
       for (int v = 0; v < kSrcVecs; ++v) unpack16<SF>(s4[c * kSrcVecs + v], x + v * (16 / kSrcVecs));
       uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float qv = rintf(x[e] / sc);  // IEEE division, round half to even
-        qv = fminf(fmaxf(qv, -127.f), 127.f);
-        const uint32_t byte = static_cast<uint32_t>(static_cast<int32_t>(qv)) & 0xFFu;
-        w[e / 4] |= byte << (8 * (e % 4));
-      }
+      for (int e = 0; e < 16; ++e) w[e / 4] |= quantise_byte<KF>(x[e], sc) << (8 * (e % 4));
       d4[c] = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
@@ -273,6 +296,14 @@ int pkv_reshape_and_cache(const void* k, const void* v, void* key_cache, void* v
       case PKV_F16: err = launch_write<PKV_F16, PKV_I8>(a, num_tokens, s); break;
       case PKV_BF16: err = launch_write<PKV_BF16, PKV_I8>(a, num_tokens, s); break;
       default: return pkv::fail(PKV_ERR_INVALID_ARG, "int8 cache takes F32/F16/BF16 rows");
+    }
+  } else if (kv_dtype == PKV_FP8) {
+    if (!k_scales || !v_scales) return pkv::fail(PKV_ERR_INVALID_ARG, "fp8 cache needs scales");
+    switch (src_dtype) {
+      case PKV_F32: err = launch_write<PKV_F32, PKV_FP8>(a, num_tokens, s); break;
+      case PKV_F16: err = launch_write<PKV_F16, PKV_FP8>(a, num_tokens, s); break;
+      case PKV_BF16: err = launch_write<PKV_BF16, PKV_FP8>(a, num_tokens, s); break;
+      default: return pkv::fail(PKV_ERR_INVALID_ARG, "fp8 cache takes F32/F16/BF16 rows");
     }
   } else {
     if (src_dtype != kv_dtype)

@@ -116,11 +116,12 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   const bool float_pair = (kv_dtype == PKV_F32 && q_dtype == PKV_F32) ||
                           (kv_dtype == PKV_F16 && q_dtype == PKV_F16) ||
                           (kv_dtype == PKV_BF16 && q_dtype == PKV_BF16);
-  const bool int8_pair = kv_dtype == PKV_I8 && (q_dtype == PKV_F16 || q_dtype == PKV_BF16);
-  if (!float_pair && !int8_pair)
+  const bool scaled_pair = (kv_dtype == PKV_I8 || kv_dtype == PKV_FP8) &&
+                           (q_dtype == PKV_F16 || q_dtype == PKV_BF16);
+  if (!float_pair && !scaled_pair)
     return pkv::fail(PKV_ERR_INVALID_ARG, "unsupported format pair q=%d kv=%d", q_dtype, kv_dtype);
-  if (int8_pair && (!k_scales || !v_scales))
-    return pkv::fail(PKV_ERR_INVALID_ARG, "int8 cache needs k_scales and v_scales");
+  if (scaled_pair && (!k_scales || !v_scales))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "int8 and fp8 caches need k_scales and v_scales");
   if (block_size != pkv_dev::kBlockSize)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d (built for %d)", block_size,
                      pkv_dev::kBlockSize);
@@ -185,6 +186,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
     case PKV_F16: err = pkv_dev::launch_decode_f16(q_dtype, head_dim, group, a, grid, s, ok); break;
     case PKV_BF16: err = pkv_dev::launch_decode_bf16(q_dtype, head_dim, group, a, grid, s, ok); break;
     case PKV_I8: err = pkv_dev::launch_decode_i8(q_dtype, head_dim, group, a, grid, s, ok); break;
+    case PKV_FP8: err = pkv_dev::launch_decode_fp8(q_dtype, head_dim, group, a, grid, s, ok); break;
     default: break;
   }
   if (!ok) return pkv::fail(PKV_ERR_UNSUPPORTED, "no kernel for this combination");

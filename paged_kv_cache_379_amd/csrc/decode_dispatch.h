@@ -15,7 +15,8 @@ constexpr int kMaxGroup = 16;  // query heads per kv head, padded to one 16-wide
 
 // Returns hipSuccess and sets ok = false when the combination is not built.
 // Multi-head attention (group 1) and fp32 caches run on the vector ALUs;
-// grouped-query attention with 16-bit or int8 caches runs on the matrix cores.
+// grouped-query attention with 16-bit, int8 or fp8 caches runs on the matrix
+// cores.
 template <int KF, int QF, int D>
 hipError_t launch_decode_groups(int group, const DecodeArgs& a, unsigned grid, hipStream_t s,
                                 bool& ok) {
@@ -56,7 +57,8 @@ hipError_t launch_decode_dims(int head_dim, int group, const DecodeArgs& a, unsi
   return hipSuccess;
 }
 
-// Defined in decode_f32.hip, decode_f16.hip, decode_bf16.hip, decode_i8.hip.
+// Defined in decode_f32.hip, decode_f16.hip, decode_bf16.hip, decode_i8.hip,
+// decode_fp8.hip.
 hipError_t launch_decode_f32(int q_dtype, int head_dim, int group, const DecodeArgs& a,
                              unsigned grid, hipStream_t s, bool& ok);
 hipError_t launch_decode_f16(int q_dtype, int head_dim, int group, const DecodeArgs& a,
@@ -65,5 +67,7 @@ hipError_t launch_decode_bf16(int q_dtype, int head_dim, int group, const Decode
                               unsigned grid, hipStream_t s, bool& ok);
 hipError_t launch_decode_i8(int q_dtype, int head_dim, int group, const DecodeArgs& a,
                             unsigned grid, hipStream_t s, bool& ok);
+hipError_t launch_decode_fp8(int q_dtype, int head_dim, int group, const DecodeArgs& a,
+                             unsigned grid, hipStream_t s, bool& ok);
 
 }  // namespace pkv_dev

@@ -133,6 +133,30 @@ template <> __device__ __forceinline__ u32x2_t i8x4_to_16<PKV_BF16>(uint32_t w) 
   return u32x2_t{Mfma<PKV_BF16>::pack(x[0], x[1]), Mfma<PKV_BF16>::pack(x[2], x[3])};
 }
 
+// Four FP8 E4M3 codes -> four exact 16-bit values, with the gfx950
+// scaled conversions at scale 1 (two codes per instruction; every E4M3 value
+// is exactly an f16 and a bf16 value).
+template <int QF> __device__ __forceinline__ u32x2_t fp8x4_to_16(uint32_t w);
+
+template <> __device__ __forceinline__ u32x2_t fp8x4_to_16<PKV_F16>(uint32_t w) {
+  return u32x2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true))};
+}
+
+template <> __device__ __forceinline__ u32x2_t fp8x4_to_16<PKV_BF16>(uint32_t w) {
+  return u32x2_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+
+// Four one-byte codes of cache format KF -> 16-bit values of format QF.
+template <int KF, int QF>
+__device__ __forceinline__ u32x2_t codes4_to_16(uint32_t w) {
+  if constexpr (KF == PKV_I8)
+    return i8x4_to_16<QF>(w);
+  else
+    return fp8x4_to_16<QF>(w);
+}
+
 template <int KF, int QF, int D>
 struct GqaTile {
   static constexpr int kEB = Format<KF>::kBytes;      // bytes per cache element (2 or 1)
@@ -143,7 +167,7 @@ struct GqaTile {
   static constexpr int kTile = kBlockSize * kPitch;   // one block of K (or V) in LDS
   static constexpr int kSlices = D / 32;              // QK^T MFMAs (32 dims each)
   static constexpr int kTiles = D / 16;               // PV MFMAs (16 dims each)
-  static_assert(KF == PKV_I8 || KF == QF, "16-bit caches are read in the query's format");
+  static_assert(scaled_format(KF) || KF == QF, "16-bit caches are read in the query's format");
   static_assert(kLoads >= 1 && kSrcRow % 64 == 0, "head_dim must fill 64-byte row slices");
 };
 
@@ -178,11 +202,11 @@ __device__ __forceinline__ void gqa_stage(uint8_t* tile, const GqaStage<KF, QF, 
   using T = GqaTile<KF, QF, D>;
 #pragma unroll
   for (int c = 0; c < T::kLoads; ++c) {
-    if constexpr (KF == PKV_I8) {
-      const u32x2_t k0 = i8x4_to_16<QF>(r.k[c].x), k1 = i8x4_to_16<QF>(r.k[c].y);
-      const u32x2_t k2 = i8x4_to_16<QF>(r.k[c].z), k3 = i8x4_to_16<QF>(r.k[c].w);
-      const u32x2_t v0 = i8x4_to_16<QF>(r.v[c].x), v1 = i8x4_to_16<QF>(r.v[c].y);
-      const u32x2_t v2 = i8x4_to_16<QF>(r.v[c].z), v3 = i8x4_to_16<QF>(r.v[c].w);
+    if constexpr (scaled_format(KF)) {
+      const u32x2_t k0 = codes4_to_16<KF, QF>(r.k[c].x), k1 = codes4_to_16<KF, QF>(r.k[c].y);
+      const u32x2_t k2 = codes4_to_16<KF, QF>(r.k[c].z), k3 = codes4_to_16<KF, QF>(r.k[c].w);
+      const u32x2_t v0 = codes4_to_16<KF, QF>(r.v[c].x), v1 = codes4_to_16<KF, QF>(r.v[c].y);
+      const u32x2_t v2 = codes4_to_16<KF, QF>(r.v[c].z), v3 = codes4_to_16<KF, QF>(r.v[c].w);
       *reinterpret_cast<u32x4_t*>(tile + soff[c]) = u32x4_t{k0.x, k0.y, k1.x, k1.y};
       *reinterpret_cast<u32x4_t*>(tile + soff[c] + 16) = u32x4_t{k2.x, k2.y, k3.x, k3.y};
       *reinterpret_cast<u32x4_t*>(tile + T::kTile + soff[c]) = u32x4_t{v0.x, v0.y, v1.x, v1.y};
@@ -416,7 +440,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
     if (kk < nk) {
       tb = (k0 == 0 && early_table) ? tb_first : trow[pb0 + wave + NW * kk];
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
-      if constexpr (KF == PKV_I8) {
+      if constexpr (scaled_format(KF)) {
         if (tb >= 0) {
           tks = a.k_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];
           tvs = a.v_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];

@@ -88,6 +88,10 @@ template <> struct Format<PKV_F32> { static constexpr int kBytes = 4; };
 template <> struct Format<PKV_F16> { static constexpr int kBytes = 2; };
 template <> struct Format<PKV_BF16> { static constexpr int kBytes = 2; };
 template <> struct Format<PKV_I8> { static constexpr int kBytes = 1; };
+template <> struct Format<PKV_FP8> { static constexpr int kBytes = 1; };
+
+// Formats whose codes carry a per-(block, kv head) scale.
+__host__ __device__ constexpr bool scaled_format(int f) { return f == PKV_I8 || f == PKV_FP8; }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -127,6 +131,22 @@ template <> __device__ __forceinline__ void unpack16<PKV_I8>(const uint4& r, flo
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       x[4 * i + j] = static_cast<float>(static_cast<int32_t>(w[i] << (24 - 8 * j)) >> 24);
+  }
+}
+
+// FP8 E4M3 codes -> fp32 with the gfx950 conversion instruction (two codes
+// per instruction; exact, every E4M3 value is an fp32 value).
+typedef float float2_t __attribute__((ext_vector_type(2)));
+template <> __device__ __forceinline__ void unpack16<PKV_FP8>(const uint4& r, float* x) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+    const float2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+    x[4 * i] = lo.x;
+    x[4 * i + 1] = lo.y;
+    x[4 * i + 2] = hi.x;
+    x[4 * i + 3] = hi.y;
   }
 }
 
@@ -404,7 +424,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     if (kk < nk) {
       tb = (k0 == 0 && early_table) ? tb_first : trow[pb0 + wave + NW * kk];
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
-      if constexpr (KF == PKV_I8) {
+      if constexpr (scaled_format(KF)) {
         if (tb >= 0) {
           tks = a.k_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];
           tvs = a.v_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];

@@ -20,6 +20,7 @@ inline int elem_bytes(int fmt) {
     case PKV_F16: return 2;
     case PKV_BF16: return 2;
     case PKV_I8: return 1;
+    case PKV_FP8: return 1;
     default: return 0;
   }
 }

@@ -31,6 +31,10 @@ Recipe (``np.random.default_rng(seed)``; draw order ctx -> pool permutation
 * an int8 cache is quantised per (physical block, kv head) with
   scale = max|x| / 127 over that block's rows (scale 1 if all are zero) and
   code = rint(x / scale) clipped to [-127, 127];
+* an fp8 (E4M3) cache likewise with scale = max|x| / 448 and the codes of
+  x / scale from torch's float8_e4m3fn conversion (a library routine: this
+  module still holds none of the method's arithmetic); fp8 codes are carried
+  as uint8;
 * the newest token of sequence s is its last context position ctx[s] - 1,
   and ``slot_mapping[s]`` names that token's cache slot.
 """
@@ -49,7 +53,10 @@ CONFIG_NAMES = {
     4: "shared_prefix_gqa_bf16",
     5: "high_concurrency_int8_gqa",
     6: "sliding_window_gqa_bf16",
+    7: "llama2_70b_fp8_mha",
+    8: "high_concurrency_fp8_gqa",
 }
+SCALED_FORMATS = ("i8", "fp8")
 
 
 @dataclass
@@ -69,7 +76,7 @@ class Workload:
     v_new: np.ndarray
     new_fmt: str
     slot_mapping: np.ndarray      # [B] int32
-    k_scales: np.ndarray = None   # [NB, Hkv] fp32 (int8 only)
+    k_scales: np.ndarray = None   # [NB, Hkv] fp32 (int8 and fp8 only)
     v_scales: np.ndarray = None
     shared_prefix_blocks: int = 0
     window: int = 0               # sliding window in tokens (0 = whole context)
@@ -135,6 +142,16 @@ def _quantise_blocks(x32):
     return codes, scales
 
 
+def _quantise_blocks_fp8(x32):
+    """fp8 E4M3 codes (uint8) and per-(block, kv head) scales for x32."""
+    import torch
+    amax = np.abs(x32).max(axis=(1, 3))
+    scales = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = np.clip(x32 / scales[:, None, :, None], -448, 448).astype(np.float32)
+    codes = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scales
+
+
 def _draw_lengths(cfg, rng, num_seqs):
     kind = cfg["ctx"][0]
     if kind == "fixed":
@@ -183,6 +200,10 @@ def _spec(index):
         return dict(num_seqs=32, num_heads=32, num_kv_heads=8, head_dim=128,
                     kv_fmt="bf16", q_fmt="bf16", ctx=("uniform", 4096, 16384),
                     pool=("factor", 1.25), max_blocks=1024, prefix=0, window=4096)
+    if index == 7:   # the 70B-shaped layer of configuration 3 with an FP8 cache
+        return dict(_spec(3), kv_fmt="fp8")
+    if index == 8:   # the high-concurrency GQA batch of configuration 5 with an FP8 cache
+        return dict(_spec(5), kv_fmt="fp8")
     raise ValueError(f"no configuration {index}")
 
 
@@ -252,7 +273,7 @@ def make_workload(index, seed=None, *, num_seqs=None, num_heads=None,
                   num_kv_heads=None, head_dim=None, ctx=None, prefix=None,
                   max_blocks=None, kv_fmt=None, q_fmt=None, block_size=BLOCK_SIZE,
                   poison_unused=False, pool=None, window=None):
-    """Draw configuration ``index`` (1..6) with optional overrides.
+    """Draw configuration ``index`` (1..8) with optional overrides.
 
     Overrides shrink or reshape a configuration for parity tests while keeping
     its structure (length mix, sharing, formats).  ``poison_unused`` fills every
@@ -276,9 +297,10 @@ def make_workload(index, seed=None, *, num_seqs=None, num_heads=None,
     q = _normal(rng, (B, H, D), q_fmt_)
     pool_shape = (nb, bs, Hkv, D)
     k_scales = v_scales = None
-    if kv_fmt_ == "i8":
-        key_cache, k_scales = _quantise_blocks(rng.standard_normal(pool_shape, dtype=np.float32))
-        value_cache, v_scales = _quantise_blocks(rng.standard_normal(pool_shape, dtype=np.float32))
+    if kv_fmt_ in SCALED_FORMATS:
+        quant = _quantise_blocks if kv_fmt_ == "i8" else _quantise_blocks_fp8
+        key_cache, k_scales = quant(rng.standard_normal(pool_shape, dtype=np.float32))
+        value_cache, v_scales = quant(rng.standard_normal(pool_shape, dtype=np.float32))
         new_fmt = q_fmt_
     else:
         key_cache = _normal(rng, pool_shape, kv_fmt_)
@@ -318,10 +340,13 @@ def used_slot_mask(wl):
 
 
 def poison(wl):
-    """Fill unread cache slots with NaN (float) or alternating +/-127 (int8)."""
+    """Fill unread cache slots with NaN (float; the NaN code 0x7F for fp8) or
+    alternating +/-127 (int8)."""
     unused = ~used_slot_mask(wl)
     for cache in (wl.key_cache, wl.value_cache):
-        if wl.kv_fmt == "i8":
+        if wl.kv_fmt == "fp8":
+            cache[unused] = np.uint8(0x7F)
+        elif wl.kv_fmt == "i8":
             cache[unused] = np.int8(127)
             cache[unused, ..., 1::2] = np.int8(-127)
         elif wl.kv_fmt == "bf16":

@@ -5,7 +5,7 @@ import torch
 import oracle.paged_attention as pa
 
 # Output tolerances (max abs error vs the fp64 oracle) per cache format.
-TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-3, "i8": 2e-2}
+TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-3, "i8": 2e-2, "fp8": 2e-3}
 # Half an ulp of the output format, relative (the output is stored in the
 # query's format, so its own rounding is part of any comparison).
 HALF_ULP = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
@@ -17,12 +17,16 @@ def to_dev(arr, fmt):
     arr = np.ascontiguousarray(arr)
     if fmt == "bf16":
         return torch.from_numpy(arr.view(np.int16)).to(DEV).view(torch.bfloat16)
+    if fmt == "fp8":
+        return torch.from_numpy(arr.view(np.uint8)).to(DEV).view(torch.float8_e4m3fn)
     return torch.from_numpy(arr).to(DEV)
 
 
 def to_host(t, fmt):
     if fmt == "bf16":
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    if fmt == "fp8":
+        return t.view(torch.uint8).cpu().numpy()
     return t.cpu().numpy()
 
 
@@ -37,7 +41,7 @@ def upload(wl):
         v_new=to_dev(wl.v_new, wl.new_fmt),
         slot_mapping=to_dev(wl.slot_mapping.astype(np.int32), "i32"),
     )
-    if wl.kv_fmt == "i8":
+    if wl.kv_fmt in ("i8", "fp8"):
         d["k_scales"] = to_dev(wl.k_scales, "f32")
         d["v_scales"] = to_dev(wl.v_scales, "f32")
     else:

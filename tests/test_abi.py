@@ -123,6 +123,9 @@ def _decode(lib, **kw):
     (dict(qf=pkv.F16, kvf=pkv.F32), pkv.ERR_INVALID_ARG),
     (dict(qf=pkv.F32, kvf=pkv.I8), pkv.ERR_INVALID_ARG),
     (dict(qf=pkv.F16, kvf=pkv.I8), pkv.ERR_INVALID_ARG),   # no scales
+    (dict(qf=pkv.F32, kvf=pkv.FP8), pkv.ERR_INVALID_ARG),
+    (dict(qf=pkv.BF16, kvf=pkv.FP8), pkv.ERR_INVALID_ARG),  # no scales
+    (dict(qf=pkv.F16, kvf=5), pkv.ERR_INVALID_ARG),
     (dict(qf=7, kvf=7), pkv.ERR_INVALID_ARG),
     (dict(bs=8), pkv.ERR_UNSUPPORTED),
     (dict(D=96), pkv.ERR_UNSUPPORTED),
@@ -154,6 +157,8 @@ def test_cache_write_and_copy_reject_bad_arguments():
     assert r(1, 1, 1, 1, None, None, None, 4, 2, 64, 16, 8, pkv.F16, pkv.F16, None) == pkv.ERR_INVALID_ARG
     assert r(1, 1, 1, 1, None, None, 1, 4, 2, 40, 16, 8, pkv.F16, pkv.F16, None) == pkv.ERR_UNSUPPORTED
     assert r(1, 1, 1, 1, None, None, 1, 0, 2, 64, 16, 8, pkv.F16, pkv.F16, None) == pkv.OK
+    assert r(1, 1, 1, 1, None, None, 1, 4, 2, 64, 16, 8, pkv.F16, pkv.FP8, None) == pkv.ERR_INVALID_ARG
+    assert r(1, 1, 1, 1, 1, 1, 1, 4, 2, 64, 16, 8, pkv.I8, pkv.FP8, None) == pkv.ERR_INVALID_ARG
     i32p = ctypes.POINTER(ctypes.c_int32)
     c = lib.pkv_copy_blocks
     bad = [np.array([[0, 9]], np.int32), np.array([[1, 2], [3, 2]], np.int32),

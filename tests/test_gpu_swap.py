@@ -10,12 +10,18 @@ from gpu_util import DEV, assert_parity, out_f64, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8}
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "i8": torch.int8,
+         "fp8": torch.float8_e4m3fn}
+SCALED = ("i8", "fp8")
 
 
 def _random_pool(rng, fmt, shape):
     if fmt == "i8":
         return torch.from_numpy(rng.integers(-127, 128, shape).astype(np.int8)).to(DEV)
+    if fmt == "fp8":   # finite codes only (0x7F and 0xFF are NaN)
+        codes = rng.integers(0, 256, shape).astype(np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x7E
+        return torch.from_numpy(codes).to(DEV).view(torch.float8_e4m3fn)
     return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(DEV).to(TORCH[fmt])
 
 
@@ -28,7 +34,7 @@ def _pinned(shape, dtype):
 
 
 @pytest.mark.parametrize("fmt,hkv,d", [("f16", 8, 128), ("bf16", 1, 64), ("f32", 2, 64),
-                                       ("i8", 4, 128)])
+                                       ("i8", 4, 128), ("fp8", 8, 128)])
 def test_swap_round_trip_bit_exact(gpu_lib, fmt, hkv, d):
     """Out: every host destination holds its device block's bytes (K, V and
     int8 scales); in: every device destination holds its host block's bytes
@@ -40,7 +46,7 @@ def test_swap_round_trip_bit_exact(gpu_lib, fmt, hkv, d):
     shape = (nb, bs, hkv, d)
     kc, vc = _random_pool(rng, fmt, shape), _random_pool(rng, fmt, shape)
     ks = vs = hks = hvs = None
-    if fmt == "i8":
+    if fmt in SCALED:
         ks = torch.from_numpy(rng.uniform(0.01, 0.1, (nb, hkv)).astype(np.float32)).to(DEV)
         vs = torch.from_numpy(rng.uniform(0.01, 0.1, (nb, hkv)).astype(np.float32)).to(DEV)
         hks, hvs = _pinned((nhb, hkv), torch.float32), _pinned((nhb, hkv), torch.float32)
@@ -56,7 +62,7 @@ def test_swap_round_trip_bit_exact(gpu_lib, fmt, hkv, d):
         assert torch.equal(hkb[h], kb[s]) and torch.equal(hvb[h], vb[s]), (s, h)
     untouched = np.setdiff1d(np.arange(nhb), dst)
     assert not hkb[untouched].any() and not hvb[untouched].any()
-    if fmt == "i8":
+    if fmt in SCALED:
         for s, h in out_pairs:
             assert torch.equal(hks[h], ks[s].cpu()) and torch.equal(hvs[h], vs[s].cpu())
     # back in, to other device blocks
@@ -101,7 +107,7 @@ def test_swap_rejects_pageable_host_memory(gpu_lib):
     assert rc == pkv.ERR_INVALID_ARG and b"pinned" in lib.pkv_last_error()
 
 
-@pytest.mark.parametrize("fmt", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "i8", "fp8"])
 def test_preempt_and_resume_decode_unchanged(gpu_lib, fmt):
     """The scheduler flow of [P1]: two of three running sequences are swapped
     out (one shares its prompt blocks with the sequence that keeps running), a
@@ -112,15 +118,16 @@ def test_preempt_and_resume_decode_unchanged(gpu_lib, fmt):
     pkv = gpu_lib
     rng = np.random.default_rng(5)
     bs, hkv, group, d, nb, nhb = 16, 2, 4, 128, 64, 40
-    qf = "f16" if fmt == "i8" else fmt
+    qf = "f16" if fmt in SCALED else fmt
     a = pkv.BlockAllocator(nb, bs)
     a.set_free_order(rng.permutation(nb))
     a.set_host_pool(nhb)
     kc, vc = _random_pool(rng, fmt, (nb, bs, hkv, d)), _random_pool(rng, fmt, (nb, bs, hkv, d))
     ks = vs = hks = hvs = None
-    if fmt == "i8":
-        ks = torch.from_numpy(rng.uniform(0.01, 0.05, (nb, hkv)).astype(np.float32)).to(DEV)
-        vs = torch.from_numpy(rng.uniform(0.01, 0.05, (nb, hkv)).astype(np.float32)).to(DEV)
+    if fmt in SCALED:
+        lo, hi = (0.01, 0.05) if fmt == "i8" else (0.001, 0.005)   # values of order 1
+        ks = torch.from_numpy(rng.uniform(lo, hi, (nb, hkv)).astype(np.float32)).to(DEV)
+        vs = torch.from_numpy(rng.uniform(lo, hi, (nb, hkv)).astype(np.float32)).to(DEV)
         hks, hvs = _pinned((nhb, hkv), torch.float32), _pinned((nhb, hkv), torch.float32)
     hk = _pinned((nhb, bs, hkv, d), TORCH[fmt])
     hv = _pinned((nhb, bs, hkv, d), TORCH[fmt])
@@ -145,12 +152,16 @@ def test_preempt_and_resume_decode_unchanged(gpu_lib, fmt):
 
     before, tables, lens = decode(seqs)
     def host(t):
-        return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
-            else t.cpu().numpy()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).cpu().numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.view(torch.uint8).cpu().numpy()
+        return t.cpu().numpy()
     ref = pa.paged_decode(host(q), qf, host(kc), host(vc), fmt, tables, lens, bs, d ** -0.5,
                           None if ks is None else ks.cpu().numpy(),
                           None if vs is None else vs.cpu().numpy())
-    assert_parity(out_f64(before), ref, fmt, label="before preemption")
+    assert_parity(out_f64(before), ref, fmt, qf, with_output_rounding=True,
+                  label="before preemption")
 
     free0 = a.num_free()
     out_pairs = a.seq_swap_out(s1) + a.seq_swap_out(s2)
@@ -164,6 +175,9 @@ def test_preempt_and_resume_decode_unchanged(gpu_lib, fmt):
     if fmt == "i8":
         kc[taken] = 127
         vc[taken] = -127
+    elif fmt == "fp8":
+        kc.view(torch.uint8)[taken] = 0x7F   # NaN codes
+        vc.view(torch.uint8)[taken] = 0xFF
     else:
         kc[taken] = float("nan")
         vc[taken] = float("nan")

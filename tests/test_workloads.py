@@ -124,3 +124,23 @@ def test_sliding_window_workload_structure():
     wl = W.make_workload(6, num_seqs=2, poison_unused=True)
     used = W.used_slot_mask(wl)
     assert used.sum() == sum(min(int(n), w) for n in wl.context_lens)
+
+
+@pytest.mark.parametrize("index,base", [(7, 3), (8, 5)])
+def test_fp8_configurations(index, base):
+    """Configurations 7 and 8 are 3 and 5 with an FP8 (E4M3) cache: the same
+    shapes and length mix; codes are finite, each (block, kv head) reaches the
+    format's largest magnitude (scale = max|x| / 448), and decoded codes times
+    the scale are of the size of the N(0, 1) draws they encode."""
+    import oracle.fp8_e4m3 as f8
+    a, b = W._spec(index), W._spec(base)
+    assert a.pop("kv_fmt") == "fp8" and b.pop("kv_fmt") != "fp8" and a == b
+    wl = W.make_workload(index, num_seqs=6, num_heads=8 if index == 7 else 32,
+                         num_kv_heads=8, max_blocks=256)
+    assert wl.key_cache.dtype == np.uint8 and wl.k_scales.shape == (wl.num_blocks, 8)
+    for cache, scales in ((wl.key_cache, wl.k_scales), (wl.value_cache, wl.v_scales)):
+        assert not ((cache & 0x7F) == 0x7F).any()
+        assert ((cache & 0x7F).max(axis=(1, 3)) == 0x7E).all()
+        vals = f8.decode(cache) * scales[:, None, :, None]
+        assert np.abs(vals).max() < 8
+    assert wl.new_fmt == wl.q_fmt == "f16"
