@@ -9,7 +9,9 @@ generator, and resident in HBM before the timed region starts.
     python bench.py [--steps K] [--warmup W] [--config 3] [--partition 0]
 
 prints ONE JSON line (``--swap`` measures preemption instead: swapping KV
-blocks to pinned host memory and back, and batched copy-on-write copies).  ``value`` is context tokens attended per second over the
+blocks to pinned host memory and back, and batched copy-on-write copies;
+``--block-size-sweep`` the decode of the configuration at block sizes 8, 16
+and 32 with the internal fragmentation of each).  ``value`` is context tokens attended per second over the
 timed steps (tokens attended per step, i.e. the context lengths or, with a
 sliding window, min(length, window), x steps / wall time between two device
 synchronisations).  ``roofline`` reports the decode call (the dominant
@@ -257,6 +259,87 @@ def swap_bench(args, torch, pkv, log):
     print(json.dumps(result), flush=True)
 
 
+def block_size_sweep(args, torch, pkv, W, log):
+    """The same workload at block sizes 8, 16 and 32 ([P1] deployment section:
+    smaller blocks waste less memory, larger ones cost the kernel less): decode
+    time and bandwidth from HIP events, table entries read, and the internal
+    fragmentation of the allocated blocks.  Prints one JSON line."""
+    dev = torch.device("cuda:0")
+    mb16 = W.make_structure(args.config)["tables"].shape[1]
+
+    def up(arr, fmt):
+        arr = np.ascontiguousarray(arr)
+        if fmt == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+        if fmt == "fp8":
+            return torch.from_numpy(arr.view(np.uint8)).to(dev).view(torch.float8_e4m3fn)
+        return torch.from_numpy(arr).to(dev)
+
+    rows = {}
+    name = None
+    for bs in (8, 16, 32):
+        wl = W.make_workload(args.config, seed=args.seed, block_size=bs,
+                             max_blocks=-(-mb16 * 16 // bs))
+        name = wl.name
+        q = up(wl.q, wl.q_fmt)
+        kc, vc = up(wl.key_cache, wl.kv_fmt), up(wl.value_cache, wl.kv_fmt)
+        tables, lens = up(wl.block_tables, "i32"), up(wl.context_lens, "i32")
+        ks = up(wl.k_scales, "f32") if wl.kv_fmt in SCALED else None
+        vs = up(wl.v_scales, "f32") if wl.kv_fmt in SCALED else None
+        out = torch.empty_like(q)
+        B, H, D = q.shape
+        MB = tables.shape[1]
+        part = pkv.decode_partition_size(B, H, wl.num_kv_heads, D, bs, MB, 0, wl.window)
+        need = pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, bs, MB, 0, wl.window)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+        def decode():
+            pkv.paged_attention_decode(out, q, kc, vc, tables, lens, bs, wl.scale, ks, vs,
+                                       workspace=ws, window=wl.window)
+
+        for _ in range(args.warmup):
+            decode()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            decode()
+            e1.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+        ab = algorithmic_bytes(wl)
+        held = tokens = 0
+        for s in range(wl.num_seqs):
+            n = int(wl.context_lens[s])
+            first = max(0, n - wl.window) if wl.window else 0
+            held += ((n + bs - 1) // bs - first // bs) * bs
+            tokens += n - first
+        err, seqs = parity_sample(wl, out, n=2)
+        gbps = ab["total"] / (us * 1e-6) / 1e9
+        rows[bs] = {"decode_us": us, "achieved_gbps": gbps, "frac_of_hbm_peak": gbps / HBM_PEAK_GBPS,
+                    "context_tokens_per_s": ab["logical_tokens"] / (us * 1e-6),
+                    "bytes_per_call": ab["total"], "partition_tokens": part,
+                    "slots_allocated": held, "tokens": tokens,
+                    "internal_fragmentation": (held - tokens) / held,
+                    "parity": {"max_abs_err": err, "seqs": seqs, "tol": TOL[wl.kv_fmt],
+                               "ok": err <= TOL[wl.kv_fmt]}}
+        log(f"block size {bs}: decode {us:.1f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%}), "
+            f"internal fragmentation {(held - tokens) / held:.2%}, parity err {err:.3g}")
+        del q, kc, vc, tables, lens, ks, vs, out, ws
+    result = {
+        "metric": "decode attention at block sizes 8/16/32: achieved HBM GB/s and internal "
+                  "fragmentation of the allocated blocks",
+        "value": rows[16]["achieved_gbps"], "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": rows[16]["decode_us"] / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": name, "block_sizes": [8, 16, 32]},
+        "sweep": {str(k): v for k, v in rows.items()},
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +355,8 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--swap", action="store_true",
                     help="measure preemption instead: swap-out/in over PCIe and batched CoW copies")
+    ap.add_argument("--block-size-sweep", action="store_true",
+                    help="measure the decode of --config at block sizes 8, 16 and 32 instead")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -295,6 +380,9 @@ def main():
 
     if args.swap:
         swap_bench(args, torch, pkv, log)
+        return
+    if args.block_size_sweep:
+        block_size_sweep(args, torch, pkv, W, log)
         return
 
     t = time.perf_counter()

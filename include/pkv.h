@@ -73,13 +73,15 @@ int pkv_abi_version(void);
 /*
  * Tokens per context partition that pkv_paged_attention_decode will use for
  * these shapes when called with the same `partition_size` (0 = automatic).
- * The result is a multiple of block_size, or 0 if the context is not split.
- * Returns 0 for invalid shapes.  The automatic choice depends on shapes only
- * (never on device data): a table of up to 160 blocks is not split, a longer
- * one is split into 64-block partitions, and the partitions are made smaller
- * until num_seqs * num_kv_heads * partitions >= 512.  With a sliding window
- * the table length is replaced by the most blocks the window can touch,
- * ceil((W - 1) / block_size) + 1, and partitions start at the window.
+ * The result is a multiple of U = max(block_size, 16), or 0 if the context is
+ * not split.  Returns 0 for invalid shapes or an unsupported block size.  The
+ * automatic choice depends on shapes only (never on device data): with
+ * span = max_blocks_per_seq * block_size rounded up to U, a span of up to 2560
+ * tokens is not split, a longer one is split into 1024-token partitions, and
+ * the partitions are made smaller (in steps of U) until
+ * num_seqs * num_kv_heads * partitions >= 512.  With a sliding window W the
+ * span is at most W + U - 1 (rounded up to U), and the partitions of a
+ * sequence start at its first attended token rounded down to U.
  */
 int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
                               int head_dim, int block_size,
@@ -105,7 +107,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  *   score_i      =   scale * dot(q[s][h], K[i][kvh])
  *   out[s][h]    =   sum_i softmax(score)_i * V[i][kvh]
  *
- * with K/V of an int8 cache dequantised as code * scale[block][kvh]
+ * with K/V of an int8 or fp8 cache dequantised as code * scale[block][kvh]
  * ([P2] "量化压缩KV Cache的INT8与FP8方案"; one scale per (block, kv head)).
  * The softmax is computed stably (scores shifted by their maximum), in fp32;
  * long contexts are split into partitions whose partial results are merged
@@ -121,15 +123,18 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  *   q            device, [B][H][D] in q_dtype: F32, F16 or BF16
  *   key_cache    device, see layout above, kv_dtype
  *   value_cache  device, same shape and format as key_cache
- *   k_scales     device fp32 [NB][Hkv], required iff kv_dtype == PKV_I8
- *   v_scales     device fp32 [NB][Hkv], required iff kv_dtype == PKV_I8
+ *   k_scales     device fp32 [NB][Hkv], required iff kv_dtype is I8 or FP8
+ *   v_scales     device fp32 [NB][Hkv], required iff kv_dtype is I8 or FP8
  *   block_tables device int32 [B][max_blocks_per_seq]
  *   context_lens device int32 [B]; values are clamped to
  *                [0, max_blocks_per_seq * block_size]
- *   kv_dtype     F32 (q F32), F16 (q F16), BF16 (q BF16), I8 (q F16 or BF16)
- *   head_dim     64 or 128; block_size 16; num_heads / num_kv_heads in
- *                {1, 2, 4, 8, 16}
- *   partition_size  tokens per partition, a multiple of block_size, or 0 for
+ *   kv_dtype     F32 (q F32), F16 (q F16), BF16 (q BF16), I8 or FP8 (q F16
+ *                or BF16)
+ *   head_dim     64 or 128; block_size 8, 16 or 32 ([P1] deployment section:
+ *                16 by default; one-byte caches with head_dim 64, block size
+ *                8 and num_heads == num_kv_heads are not built: UNSUPPORTED);
+ *                num_heads / num_kv_heads in {1, 2, 4, 8, 16}
+ *   partition_size  tokens per partition, a multiple of max(block_size, 16), or 0 for
  *                the library's choice; a value >= the longest possible context
  *                disables splitting
  *   sliding_window  0 (attend to the whole context) or W > 0 tokens

@@ -21,42 +21,45 @@ hipError_t launch_reduce(int head_dim, const DecodeArgs& a, unsigned grid, hipSt
 
 namespace {
 
-// Automatic partitioning (measured on MI355X with the five standard
-// workloads): a context of up to kWholeBlocks blocks is handled by one
+// Automatic partitioning (measured on MI355X with the standard workloads at
+// block size 16): a context of up to kWholeTokens tokens is handled by one
 // workgroup per (sequence, kv head); longer ones are split into partitions of
-// kSplitBlocks blocks, so a few long sequences among short ones do not leave a
+// kSplitTokens tokens, so a few long sequences among short ones do not leave a
 // tail of long-running workgroups.  Independently, the grid is split further
 // until it has at least kMinItems workgroups (two per CU), so small batches
-// still fill the chip.
-constexpr int kWholeBlocks = 160;  // 2560 tokens at block size 16
-constexpr int kSplitBlocks = 64;   // 1024 tokens
+// still fill the chip.  Partitions are whole multiples of
+// partition_align(block_size) tokens.
+constexpr int64_t kWholeTokens = 2560;
+constexpr int64_t kSplitTokens = 1024;
 constexpr int64_t kMinItems = 512;
 
-// Blocks per partition (max_blocks when the context is not split), or -1 for
-// an invalid request.  partition_size = 0 picks automatically.
-int partition_blocks(int num_seqs, int num_kv_heads, int max_blocks, int block_size,
-                     int partition_size) {
-  if (max_blocks <= 0 || block_size <= 0 || partition_size < 0) return -1;
-  if (partition_size > 0) {
-    if (partition_size % block_size) return -1;
-    const int pb = partition_size / block_size;
-    return pb >= max_blocks ? max_blocks : pb;
-  }
-  int pb = max_blocks > kWholeBlocks ? kSplitBlocks : max_blocks;
-  const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  if (pairs > 0 && pairs * ((max_blocks + pb - 1) / pb) < kMinItems) {
-    const int64_t parts = (kMinItems + pairs - 1) / pairs;
-    pb = static_cast<int>((max_blocks + parts - 1) / parts);
-  }
-  return pb < 1 ? 1 : (pb > max_blocks ? max_blocks : pb);
+// Tokens a context can span from its partition origin: the whole table, or
+// with a sliding window of W tokens at most W plus the rounding of the origin
+// down to the partition alignment; rounded up to whole alignment units.
+int64_t attended_tokens(int max_blocks, int block_size, int window) {
+  const int64_t u = pkv_dev::partition_align(block_size);
+  int64_t span = static_cast<int64_t>(max_blocks) * block_size;
+  if (window > 0 && window + u - 1 < span) span = window + u - 1;
+  return (span + u - 1) / u * u;
 }
 
-// Table entries a context can read: all of them, or with a sliding window of
-// W tokens at most the blocks that W consecutive tokens can touch.
-int attended_blocks(int max_blocks, int block_size, int window) {
-  if (window <= 0) return max_blocks;
-  const int64_t span = (static_cast<int64_t>(window) - 1 + block_size - 1) / block_size + 1;
-  return span < max_blocks ? static_cast<int>(span) : max_blocks;
+// Tokens per partition (equal to span when the context is not split), or -1
+// for an invalid request.  partition_size = 0 picks automatically.
+int64_t partition_tokens(int num_seqs, int num_kv_heads, int64_t span, int block_size,
+                         int partition_size) {
+  const int64_t u = pkv_dev::partition_align(block_size);
+  if (span <= 0 || partition_size < 0) return -1;
+  if (partition_size > 0) {
+    if (partition_size % u) return -1;
+    return partition_size >= span ? span : partition_size;
+  }
+  int64_t pt = span > kWholeTokens ? kSplitTokens : span;
+  const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  if (pairs > 0 && pairs * ((span + pt - 1) / pt) < kMinItems) {
+    const int64_t parts = (kMinItems + pairs - 1) / pairs;
+    pt = ((span + parts - 1) / parts + u - 1) / u * u;
+  }
+  return pt < u ? u : (pt > span ? span : pt);
 }
 
 bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
@@ -73,24 +76,26 @@ int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads, int
                               int block_size, int max_blocks_per_seq, int partition_size,
                               int sliding_window) {
   if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
-      sliding_window < 0)
+      sliding_window < 0 || !pkv_dev::supported_block_size(block_size) ||
+      static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
     return 0;
-  const int eff = attended_blocks(max_blocks_per_seq, block_size, sliding_window);
-  const int pb = partition_blocks(num_seqs, num_kv_heads, eff, block_size, partition_size);
-  if (pb <= 0 || pb >= eff) return 0;
-  return pb * block_size;
+  const int64_t span = attended_tokens(max_blocks_per_seq, block_size, sliding_window);
+  const int64_t pt = partition_tokens(num_seqs, num_kv_heads, span, block_size, partition_size);
+  if (pt <= 0 || pt >= span) return 0;
+  return static_cast<int>(pt);
 }
 
 size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                  int block_size, int max_blocks_per_seq, int partition_size,
                                  int sliding_window) {
   if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
-      sliding_window < 0)
+      sliding_window < 0 || !pkv_dev::supported_block_size(block_size) ||
+      static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
     return 0;
-  const int eff = attended_blocks(max_blocks_per_seq, block_size, sliding_window);
-  const int pb = partition_blocks(num_seqs, num_kv_heads, eff, block_size, partition_size);
-  if (pb <= 0 || pb >= eff) return 0;
-  const size_t parts = (eff + pb - 1) / pb;
+  const int64_t span = attended_tokens(max_blocks_per_seq, block_size, sliding_window);
+  const int64_t pt = partition_tokens(num_seqs, num_kv_heads, span, block_size, partition_size);
+  if (pt <= 0 || pt >= span) return 0;
+  const size_t parts = static_cast<size_t>((span + pt - 1) / pt);
   return static_cast<size_t>(num_seqs) * num_heads * parts * (head_dim + 2) * sizeof(float);
 }
 
@@ -122,9 +127,6 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
     return pkv::fail(PKV_ERR_INVALID_ARG, "unsupported format pair q=%d kv=%d", q_dtype, kv_dtype);
   if (scaled_pair && (!k_scales || !v_scales))
     return pkv::fail(PKV_ERR_INVALID_ARG, "int8 and fp8 caches need k_scales and v_scales");
-  if (block_size != pkv_dev::kBlockSize)
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d (built for %d)", block_size,
-                     pkv_dev::kBlockSize);
   if (head_dim != 64 && head_dim != 128)
     return pkv::fail(PKV_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", head_dim);
   const int group = num_heads / num_kv_heads;
@@ -135,12 +137,14 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
     return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
   if (sliding_window < 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "sliding_window %d is negative", sliding_window);
-  const int eff = attended_blocks(max_blocks_per_seq, block_size, sliding_window);
-  const int pb = partition_blocks(num_seqs, num_kv_heads, eff, block_size, partition_size);
-  if (pb <= 0)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a multiple of block_size %d",
-                     partition_size, block_size);
-  const int parts = (eff + pb - 1) / pb;
+  if (!pkv_dev::supported_block_size(block_size))
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d (8, 16 or 32)", block_size);
+  const int64_t span = attended_tokens(max_blocks_per_seq, block_size, sliding_window);
+  const int64_t pt = partition_tokens(num_seqs, num_kv_heads, span, block_size, partition_size);
+  if (pt <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a multiple of %d tokens",
+                     partition_size, pkv_dev::partition_align(block_size));
+  const int parts = static_cast<int>((span + pt - 1) / pt);
   const size_t need =
       pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                 max_blocks_per_seq, partition_size, sliding_window);
@@ -172,7 +176,9 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   a.num_kv_heads = num_kv_heads;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = num_blocks;
-  a.part_blocks = pb;
+  a.block_size = block_size;
+  a.align = pkv_dev::partition_align(block_size);
+  a.part_tokens = static_cast<int>(pt);
   a.num_parts = parts;
   a.window = sliding_window;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);

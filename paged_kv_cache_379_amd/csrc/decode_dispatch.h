@@ -17,29 +17,39 @@ constexpr int kMaxGroup = 16;  // query heads per kv head, padded to one 16-wide
 // Multi-head attention (group 1) and fp32 caches run on the vector ALUs;
 // grouped-query attention with 16-bit, int8 or fp8 caches runs on the matrix
 // cores.
-template <int KF, int QF, int D>
+template <int KF, int QF, int D, int G, int BS>
+hipError_t launch_vector(const DecodeArgs& a, unsigned grid, hipStream_t s, bool& ok) {
+  if constexpr (DecodeTile<KF, QF, D, G, kDecodeWaves, BS>::kBuilt) {
+    ok = true;
+    hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, G, kDecodeWaves, BS>), dim3(grid),
+                       dim3(kDecodeWaves * 64), 0, s, a);
+    return hipGetLastError();
+  } else {
+    ok = false;
+    return hipSuccess;
+  }
+}
+
+template <int KF, int QF, int D, int BS>
 hipError_t launch_decode_groups(int group, const DecodeArgs& a, unsigned grid, hipStream_t s,
                                 bool& ok) {
   ok = true;
   const dim3 g(grid), b(kDecodeWaves * 64);
   if constexpr (KF == PKV_F32) {
     switch (group) {
-      case 1: hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, 1, kDecodeWaves>), g, b, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, 2, kDecodeWaves>), g, b, 0, s, a); break;
-      case 4: hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, 4, kDecodeWaves>), g, b, 0, s, a); break;
-      case 8: hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, 8, kDecodeWaves>), g, b, 0, s, a); break;
-      case 16: hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, 16, kDecodeWaves>), g, b, 0, s, a); break;
+      case 1: return launch_vector<KF, QF, D, 1, BS>(a, grid, s, ok);
+      case 2: return launch_vector<KF, QF, D, 2, BS>(a, grid, s, ok);
+      case 4: return launch_vector<KF, QF, D, 4, BS>(a, grid, s, ok);
+      case 8: return launch_vector<KF, QF, D, 8, BS>(a, grid, s, ok);
+      case 16: return launch_vector<KF, QF, D, 16, BS>(a, grid, s, ok);
       default: ok = false; return hipSuccess;
     }
   } else {
-    if (group == 1) {
-      hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, 1, kDecodeWaves>), g, b, 0, s, a);
-    } else if (group >= 2 && group <= 8) {
-      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, true>),
-                         g, b, 0, s, a);
+    if (group == 1) return launch_vector<KF, QF, D, 1, BS>(a, grid, s, ok);
+    if (group >= 2 && group <= 8) {
+      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, true, BS>), g, b, 0, s, a);
     } else if (group > 8 && group <= kMaxGroup) {
-      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, false>),
-                         g, b, 0, s, a);
+      hipLaunchKernelGGL((paged_decode_gqa_kernel<KF, QF, D, kDecodeWaves, false, BS>), g, b, 0, s, a);
     } else {
       ok = false;
       return hipSuccess;
@@ -48,11 +58,22 @@ hipError_t launch_decode_groups(int group, const DecodeArgs& a, unsigned grid, h
   return hipGetLastError();
 }
 
+template <int KF, int QF, int D>
+hipError_t launch_decode_block(int group, int block_size, const DecodeArgs& a, unsigned grid,
+                               hipStream_t s, bool& ok) {
+  switch (block_size) {
+    case 8: return launch_decode_groups<KF, QF, D, 8>(group, a, grid, s, ok);
+    case 16: return launch_decode_groups<KF, QF, D, 16>(group, a, grid, s, ok);
+    case 32: return launch_decode_groups<KF, QF, D, 32>(group, a, grid, s, ok);
+    default: ok = false; return hipSuccess;
+  }
+}
+
 template <int KF, int QF>
 hipError_t launch_decode_dims(int head_dim, int group, const DecodeArgs& a, unsigned grid,
                               hipStream_t s, bool& ok) {
-  if (head_dim == 64) return launch_decode_groups<KF, QF, 64>(group, a, grid, s, ok);
-  if (head_dim == 128) return launch_decode_groups<KF, QF, 128>(group, a, grid, s, ok);
+  if (head_dim == 64) return launch_decode_block<KF, QF, 64>(group, a.block_size, a, grid, s, ok);
+  if (head_dim == 128) return launch_decode_block<KF, QF, 128>(group, a.block_size, a, grid, s, ok);
   ok = false;
   return hipSuccess;
 }

@@ -157,6 +157,11 @@ __device__ __forceinline__ u32x2_t codes4_to_16(uint32_t w) {
     return fp8x4_to_16<QF>(w);
 }
 
+// The grouped-query kernel works in tiles of 16 tokens, the MFMA tile height:
+// a tile is one 16-token block, half of a 32-token block, or two 8-token
+// blocks.
+constexpr int kTileRows = 16;
+
 template <int KF, int QF, int D>
 struct GqaTile {
   static constexpr int kEB = Format<KF>::kBytes;      // bytes per cache element (2 or 1)
@@ -164,34 +169,40 @@ struct GqaTile {
   static constexpr int kSrcLanesPerRow = kSrcRow / 16;
   static constexpr int kLoads = kSrcRow / 64;         // 16-byte loads per lane per K (or V) block
   static constexpr int kPitch = 2 * D + 16;           // LDS row pitch (16-bit elements + pad)
-  static constexpr int kTile = kBlockSize * kPitch;   // one block of K (or V) in LDS
+  static constexpr int kTile = kTileRows * kPitch;    // one tile of K (or V) in LDS
   static constexpr int kSlices = D / 32;              // QK^T MFMAs (32 dims each)
   static constexpr int kTiles = D / 16;               // PV MFMAs (16 dims each)
   static_assert(scaled_format(KF) || KF == QF, "16-bit caches are read in the query's format");
   static_assert(kLoads >= 1 && kSrcRow % 64 == 0, "head_dim must fill 64-byte row slices");
 };
 
-// One block's K and V as each lane loads them: load c covers source bytes
-// 16 * (64c + lane) of the block's rows of one kv head, in row order.
+// One tile's K and V as each lane loads them: load c covers source bytes
+// 16 * (64c + lane) of the tile's rows of one kv head, in row order.
 template <int KF, int QF, int D>
 struct GqaStage {
   u32x4_t k[GqaTile<KF, QF, D>::kLoads];
   u32x4_t v[GqaTile<KF, QF, D>::kLoads];
 };
 
-template <int KF, int QF, int D>
+// off_a: byte offset of the tile's first row (block and row within it);
+// with two blocks per tile (TWO), rows 8..15 come from off_b instead
+// (second[c] says which half this lane's load c reads).
+template <int KF, int QF, int D, bool TWO>
 __device__ __forceinline__ void gqa_load(GqaStage<KF, QF, D>& r, const uint8_t* kbase,
-                                         const uint8_t* vbase, int64_t blk_stride, int phys,
-                                         const uint32_t (&goff)[GqaTile<KF, QF, D>::kLoads]) {
+                                         const uint8_t* vbase, int64_t off_a, int64_t off_b,
+                                         const uint32_t (&goff)[GqaTile<KF, QF, D>::kLoads],
+                                         const bool (&second)[GqaTile<KF, QF, D>::kLoads]) {
   using T = GqaTile<KF, QF, D>;
-  const uint8_t* kp = kbase + static_cast<int64_t>(phys) * blk_stride;
-  const uint8_t* vp = vbase + static_cast<int64_t>(phys) * blk_stride;
 #pragma unroll
-  for (int c = 0; c < T::kLoads; ++c)
-    r.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + goff[c]));
+  for (int c = 0; c < T::kLoads; ++c) {
+    const int64_t off = (TWO && second[c]) ? off_b : off_a;
+    r.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kbase + off + goff[c]));
+  }
 #pragma unroll
-  for (int c = 0; c < T::kLoads; ++c)
-    r.v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vp + goff[c]));
+  for (int c = 0; c < T::kLoads; ++c) {
+    const int64_t off = (TWO && second[c]) ? off_b : off_a;
+    r.v[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vbase + off + goff[c]));
+  }
 }
 
 // Staged registers -> the wave's LDS tiles (K, then V) in 16-bit form.
@@ -225,9 +236,10 @@ struct GqaState {
   f32x4_t acc[GqaTile<KF, QF, D>::kTiles];  // O^T: dims 16c + 4g + i, column t
 };
 
-// Scores, online softmax and weighted V sum of one block staged in `tile`
-// (valid tokens < 16 only in the last block of a context).  SPLIT: G <= 8 and
-// the lo halves of the weights use columns 8..15.
+// Scores, online softmax and weighted V sum of one tile staged in `tile`
+// (rows outside lo <= row < valid are masked).  ksc and vsc are this lane's
+// int8/fp8 scales (its tokens 4g .. 4g + 3 lie in one block).  SPLIT: G <= 8
+// and the lo halves of the weights use columns 8..15.
 template <int KF, int QF, int D, bool SPLIT>
 __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* tile,
                                             const u32x4_t (&qop)[GqaTile<KF, QF, D>::kSlices],
@@ -235,10 +247,10 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
                                             float scale_log2) {
   using T = GqaTile<KF, QF, D>;
   using M = Mfma<QF>;
-  // Rows outside the attended tokens lo <= offset < valid (lo > 0 only in the
-  // first block of a sliding window): zero their V elements (this lane's
-  // 16-byte chunks of row t) so the weighted sum never touches those slots.
-  if (valid < kBlockSize || lo > 0) {
+  // Rows outside the attended tokens lo <= offset < valid: zero their V
+  // elements (this lane's 16-byte chunks of row t) so the weighted sum never
+  // touches those slots.
+  if (valid < kTileRows || lo > 0) {
     if (t >= valid || t < lo) {
 #pragma unroll
       for (int c = 0; c < T::kSlices; ++c)
@@ -334,9 +346,24 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
   }
 }
 
-template <int KF, int QF, int D, int NW, bool SPLIT>
+template <int KF, int QF, int D, int NW, bool SPLIT, int BS>
 __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a) {
   using T = GqaTile<KF, QF, D>;
+  constexpr bool kTwo = BS < kTileRows;                     // two blocks per tile
+  constexpr int kTilesPerBlock = BS > kTileRows ? BS / kTileRows : 1;
+  static_assert(BS == 8 || BS % kTileRows == 0, "block size");
+  const int part_tiles = a.part_tokens / kTileRows;
+  // Table entries of tile jj (the second only with two blocks per tile; -1
+  // past the table row).
+  auto tile_entries = [&](const int32_t* row, int jj, int& ea, int& eb) {
+    if constexpr (kTwo) {
+      ea = row[2 * jj];
+      eb = 2 * jj + 1 < a.max_blocks ? row[2 * jj + 1] : -1;
+    } else {
+      ea = row[jj / kTilesPerBlock];
+      eb = -1;
+    }
+  };
 
   // Per-wave K/V tiles during the loop; the same bytes then hold the waves'
   // accumulators for the final merge.
@@ -374,12 +401,13 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
   // With a sliding window the partitions start at the window, which depends
   // on the length, so the table is read after it.
   const bool early_table = a.window == 0;
-  int tb_first = -1;
+  const int max_tiles = (a.max_blocks * BS + kTileRows - 1) / kTileRows;
+  int tb_first = -1, tb_first_b = -1;
   if (early_table) {
-    const int pb0e = part * a.part_blocks;
-    const int span_full = min(pb0e + a.part_blocks, a.max_blocks) - pb0e - wave;
+    const int pt0e = part * part_tiles;
+    const int span_full = min(pt0e + part_tiles, max_tiles) - pt0e - wave;
     const int nk_full = span_full > 0 ? (span_full + NW - 1) / NW : 0;
-    if (lane < min(64, nk_full)) tb_first = trow[pb0e + wave + NW * lane];
+    if (lane < min(64, nk_full)) tile_entries(trow, pt0e + wave + NW * lane, tb_first, tb_first_b);
   }
 
   // Q^T operand: head t of this kv head's group (head t % 8 when SPLIT, so
@@ -399,11 +427,10 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
 
   const Span sp = attended_span(a, seq);
   const int ctx = sp.ctx;
-  const int pb0 = sp.first_block + part * a.part_blocks;
-  if (pb0 >= sp.end_block && part != 0) return;  // partition past the context
-  const int pb1 = min(pb0 + a.part_blocks, sp.end_block);
-  const int nparts_seq = (sp.end_block - sp.first_block + a.part_blocks - 1) / a.part_blocks;
-  const bool direct = nparts_seq <= 1;
+  if (part >= sp.nparts && part != 0) return;  // partition past the context
+  const int pt0 = sp.origin / kTileRows + part * part_tiles;
+  const int pt1 = min(pt0 + part_tiles, (ctx + kTileRows - 1) / kTileRows);
+  const bool direct = sp.nparts <= 1;
 
   GqaState<KF, QF, D> st;
   st.m = -INFINITY;
@@ -412,64 +439,103 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
   for (int c = 0; c < T::kTiles; ++c) st.acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * T::kSrcRow;
-  const int64_t blk_stride = row_stride * kBlockSize;
+  const int64_t blk_stride = row_stride * BS;
   const int64_t head_off = static_cast<int64_t>(kvh) * T::kSrcRow;
   const uint8_t* kbase = a.key_cache + head_off;
   const uint8_t* vbase = a.value_cache + head_off;
   uint8_t* tile = smem + wave * 2 * T::kTile;
-  // Per load c: global byte offset of this lane's 16 source bytes inside a
-  // block (from the kv head's row 0), and the LDS offset of their 16-bit form.
+  // Per load c: global byte offset of this lane's 16 source bytes from the
+  // first row of its block's part of the tile, whether that is the tile's
+  // second block (two blocks per tile), and the LDS offset of their 16-bit
+  // form.
   uint32_t goff[T::kLoads], soff[T::kLoads];
+  bool second[T::kLoads];
 #pragma unroll
   for (int c = 0; c < T::kLoads; ++c) {
     const int idx = 64 * c + lane;
     const int r = idx / T::kSrcLanesPerRow;
     const int ch = idx % T::kSrcLanesPerRow;
-    goff[c] = static_cast<uint32_t>(r * row_stride + 16 * ch);
+    second[c] = kTwo && r >= BS;
+    goff[c] = static_cast<uint32_t>((kTwo ? r % BS : r) * row_stride + 16 * ch);
     soff[c] = static_cast<uint32_t>(r * T::kPitch + 16 * ch * (2 / T::kEB));
   }
 
-  // Blocks of this wave: pb0 + wave + NW * k for k < nk.  The loads of block
-  // k + 1 are in flight while block k is computed from the LDS tiles.
-  const int span = pb1 - pb0 - wave;
+  // Tiles of this wave: pt0 + wave + NW * k for k < nk.  The loads of tile
+  // k + 1 are in flight while tile k is computed from the LDS tiles.
+  const int span = pt1 - pt0 - wave;
   const int nk = span > 0 ? (span + NW - 1) / NW : 0;
   for (int k0 = 0; k0 < nk; k0 += 64) {
     const int kk = k0 + lane;
-    int tb = -1;
-    float tks = 1.f, tvs = 1.f;
+    int tb = -1, tb2 = -1;
+    float tks = 1.f, tvs = 1.f, tks2 = 1.f, tvs2 = 1.f;
     if (kk < nk) {
-      tb = (k0 == 0 && early_table) ? tb_first : trow[pb0 + wave + NW * kk];
+      if (k0 == 0 && early_table) {
+        tb = tb_first;
+        tb2 = tb_first_b;
+      } else {
+        tile_entries(trow, pt0 + wave + NW * kk, tb, tb2);
+      }
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
+      if (static_cast<unsigned>(tb2) >= static_cast<unsigned>(a.num_blocks)) tb2 = -1;
       if constexpr (scaled_format(KF)) {
         if (tb >= 0) {
           tks = a.k_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];
           tvs = a.v_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];
         }
+        if (kTwo && tb2 >= 0) {
+          tks2 = a.k_scales[static_cast<int64_t>(tb2) * a.num_kv_heads + kvh];
+          tvs2 = a.v_scales[static_cast<int64_t>(tb2) * a.num_kv_heads + kvh];
+        }
       }
     }
     const int kend = min(64, nk - k0);
-    // Physical id of block k of this chunk (0 if the entry is out of range; the
-    // block is then fully masked).
-    auto phys_of = [&](int k) {
+    // Byte offsets of tile k's rows (its block, or its two blocks; 0 for an
+    // entry outside the pool, whose rows are then masked).
+    auto offsets = [&](int k, int64_t& off_a, int64_t& off_b) {
       const int p = __builtin_amdgcn_readlane(tb, k);
-      return p < 0 ? 0 : p;
+      off_a = static_cast<int64_t>(p < 0 ? 0 : p) * blk_stride;
+      off_b = 0;
+      if constexpr (kTwo) {
+        const int p2 = __builtin_amdgcn_readlane(tb2, k);
+        off_b = static_cast<int64_t>(p2 < 0 ? 0 : p2) * blk_stride;
+      } else if constexpr (kTilesPerBlock > 1) {
+        const int jj = pt0 + wave + NW * (k0 + k);
+        off_a += static_cast<int64_t>((jj % kTilesPerBlock) * kTileRows) * row_stride;
+      }
     };
-    // Block k of this chunk, already staged in LDS: scores, softmax, weighted sum.
+    // Tile k of this chunk, already staged in LDS: scores, softmax, weighted sum.
     auto compute = [&](int k) {
       const int p = __builtin_amdgcn_readlane(tb, k);
-      const int j = pb0 + wave + NW * (k0 + k);
-      const int lo = max(0, sp.first - j * kBlockSize);
-      const int valid = p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize);
-      const float ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k));
-      const float vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k));
+      const int jj = pt0 + wave + NW * (k0 + k);
+      int lo = max(0, sp.first - jj * kTileRows);
+      int valid = min(kTileRows, ctx - jj * kTileRows);
+      float ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k));
+      float vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k));
+      if constexpr (kTwo) {
+        const int p2 = __builtin_amdgcn_readlane(tb2, k);
+        if (p < 0) lo = max(lo, BS);
+        if (p2 < 0) valid = min(valid, BS);
+        // lane (t, g) holds tokens 4g .. 4g + 3: rows 8..15 (g >= 2) are the
+        // second block's
+        if (4 * g >= BS) {
+          ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks2), k));
+          vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs2), k));
+        }
+      } else {
+        if (p < 0) valid = 0;
+      }
       gqa_compute<KF, QF, D, SPLIT>(st, tile, qop, lo, valid, ks, vs, t, g, a.scale_log2);
     };
-    // The loads of block k + 1 are in flight while block k is computed.
     GqaStage<KF, QF, D> r0;
-    gqa_load(r0, kbase, vbase, blk_stride, phys_of(0), goff);
+    int64_t oa, ob;
+    offsets(0, oa, ob);
+    gqa_load<KF, QF, D, kTwo>(r0, kbase, vbase, oa, ob, goff, second);
     for (int k = 0; k < kend; ++k) {
       gqa_stage(tile, r0, soff);
-      if (k + 1 < kend) gqa_load(r0, kbase, vbase, blk_stride, phys_of(k + 1), goff);
+      if (k + 1 < kend) {
+        offsets(k + 1, oa, ob);
+        gqa_load<KF, QF, D, kTwo>(r0, kbase, vbase, oa, ob, goff, second);
+      }
       compute(k);
     }
   }

@@ -8,7 +8,7 @@
 //
 // What is computed ([P1] "PagedAttention注意力计算流程" and its kernel sketch):
 // for a sequence's query head, token i of the context lives in physical block
-// table[i / 16] at offset i % 16; its score is scale * dot(q, k_i); the output
+// table[i / bs] at offset i % bs; its score is scale * dot(q, k_i); the output
 // is the softmax-weighted sum of the v_i.  [P3] section 三 notes that the
 // scattered rows are best walked block by block, reading each block's rows
 // contiguously; that is what the wave loop below does.
@@ -20,7 +20,7 @@
 //   * the waves of a workgroup take the partition's blocks round-robin; a wave
 //     reads a block's K rows of its kv head with 16-byte loads, LPR lanes per
 //     row (a 256-byte fp16 row of head_dim 128 is 16 lanes), RPI rows per load
-//     instruction, IPB instructions per 16-token block, then the same for V;
+//     instruction, IPB instructions per block of BS tokens, then the same for V;
 //   * each lane holds its E query elements (per head) in registers, the dot
 //     product is finished by a DPP butterfly across the LPR lanes of a row;
 //   * every row group of a wave (the lanes that share token rows) keeps its own
@@ -41,7 +41,14 @@
 
 namespace pkv_dev {
 
-constexpr int kBlockSize = 16;
+// Block sizes the kernels are built for ([P1] "PagedAttention分页内存管理原理"
+// uses 16; 8 and 32 are the neighbours its block-size trade-off discusses).
+__host__ __device__ constexpr bool supported_block_size(int bs) {
+  return bs == 8 || bs == 16 || bs == 32;
+}
+// Partitions start at multiples of this many tokens: a whole block and a whole
+// 16-token MFMA tile of the grouped-query kernel.
+__host__ __device__ constexpr int partition_align(int bs) { return bs > 16 ? bs : 16; }
 
 struct DecodeArgs {
   void* out;
@@ -59,7 +66,9 @@ struct DecodeArgs {
   int num_kv_heads;
   int max_blocks;
   int num_blocks;
-  int part_blocks;  // blocks per partition
+  int block_size;   // tokens per block (the kernel's BS)
+  int align;        // partition_align(block_size)
+  int part_tokens;  // tokens per partition, a multiple of align
   int num_parts;    // partitions per sequence in the grid
   int window;       // sliding window in tokens, 0 = the whole context
   float scale_log2; // scale * log2(e)
@@ -67,20 +76,24 @@ struct DecodeArgs {
 
 // The attended part of a sequence's context: its length clamped to the table,
 // the first attended token (the last `window` tokens when a sliding window is
-// set) and the logical blocks [first_block, end_block) that hold them.
-// Partition p covers blocks first_block + p * part_blocks onwards.
+// set), the origin of its partitions (the first token rounded down to the
+// partition alignment) and the number of partitions that hold tokens.
+// Partition p covers tokens origin + p * part_tokens onwards.
 struct Span {
   int ctx;
   int first;
-  int first_block;
-  int end_block;
+  int origin;
+  int nparts;
 };
 
 __device__ __forceinline__ Span attended_span(const DecodeArgs& a, int seq) {
+  const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[seq];
-  ctx = ctx < 0 ? 0 : (ctx > a.max_blocks * kBlockSize ? a.max_blocks * kBlockSize : ctx);
+  ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
   const int first = a.window > 0 ? max(0, ctx - a.window) : 0;
-  return Span{ctx, first, first / kBlockSize, (ctx + kBlockSize - 1) / kBlockSize};
+  const int origin = first / a.align * a.align;
+  const int nparts = ctx > origin ? (ctx - origin + a.part_tokens - 1) / a.part_tokens : 0;
+  return Span{ctx, first, origin, nparts};
 }
 
 template <int F> struct Format;
@@ -228,16 +241,18 @@ __device__ __forceinline__ float across_groups_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int KF, int QF, int D, int G, int NW>
+template <int KF, int QF, int D, int G, int NW, int BS>
 struct DecodeTile {
   static constexpr int kEB = Format<KF>::kBytes;
   static constexpr int kRow = D * kEB;        // bytes of one (token, kv head) row
   static constexpr int kLPR = kRow / 16;      // lanes per row
   static constexpr int kRPI = 64 / kLPR;      // rows per load instruction
-  static constexpr int kIPB = kBlockSize / kRPI;  // load instructions per block
+  static constexpr int kIPB = BS / kRPI;      // load instructions per block
   static constexpr int kE = 16 / kEB;         // elements per lane per load
+  // Whether one load instruction's rows fit in a block (not so for one-byte
+  // rows of head_dim 64 in 8-token blocks: that combination is not built).
+  static constexpr bool kBuilt = kRPI <= BS && BS % kRPI == 0;
   static_assert(kRow % 16 == 0 && kLPR >= 1 && kLPR <= 64 && 64 % kLPR == 0, "row shape");
-  static_assert(kRPI <= kBlockSize && kBlockSize % kRPI == 0, "block shape");
 };
 
 // Per-lane running softmax state of one row group for G heads.
@@ -249,14 +264,14 @@ struct SoftmaxState {
 };
 
 // Score, mask and accumulate NBLK blocks whose loads are issued together.
-template <int KF, int QF, int D, int G, int NW, int NBLK>
+template <int KF, int QF, int D, int G, int NW, int BS, int NBLK>
 __device__ __forceinline__ void process_blocks(
-    SoftmaxState<G, DecodeTile<KF, QF, D, G, NW>::kE>& st,
-    const float (&qf)[G][DecodeTile<KF, QF, D, G, NW>::kE], const uint8_t* kbase,
+    SoftmaxState<G, DecodeTile<KF, QF, D, G, NW, BS>::kE>& st,
+    const float (&qf)[G][DecodeTile<KF, QF, D, G, NW, BS>::kE], const uint8_t* kbase,
     const uint8_t* vbase, int64_t blk_stride, int64_t row_stride, const int (&phys)[NBLK],
     const int (&lo)[NBLK], const int (&valid)[NBLK], const float (&ksc)[NBLK],
     const float (&vsc)[NBLK], int rg, float scale_log2) {
-  using T = DecodeTile<KF, QF, D, G, NW>;
+  using T = DecodeTile<KF, QF, D, G, NW, BS>;
   constexpr int E = T::kE, IPB = T::kIPB, RPI = T::kRPI, LPR = T::kLPR;
   uint4 kr[NBLK][IPB], vr[NBLK][IPB];
 #pragma unroll
@@ -291,7 +306,7 @@ __device__ __forceinline__ void process_blocks(
     const float sc = scale_log2 * ksc[b];
     // tokens lo <= offset < valid of the block are attended (lo > 0 only in
     // the first block of a sliding window)
-    const bool partial = valid[b] < kBlockSize || lo[b] > 0;
+    const bool partial = valid[b] < BS || lo[b] > 0;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -341,11 +356,13 @@ __device__ __forceinline__ void process_blocks(
   }
 }
 
-template <int KF, int QF, int D, int G, int NW>
+template <int KF, int QF, int D, int G, int NW, int BS>
 __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
-  using T = DecodeTile<KF, QF, D, G, NW>;
+  using T = DecodeTile<KF, QF, D, G, NW, BS>;
   constexpr int E = T::kE, LPR = T::kLPR;
-  constexpr int UNROLL = 2;
+  // Blocks whose loads are issued together: 32 tokens' worth.
+  constexpr int UNROLL = BS >= 32 ? 1 : 32 / BS;
+  const int part_blocks = a.part_tokens / BS;
 
   __shared__ float s_acc[NW][G][D];
   __shared__ float s_m[NW][G];
@@ -378,8 +395,8 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   const bool early_table = a.window == 0;
   int tb_first = -1;
   if (early_table) {
-    const int pb0e = part * a.part_blocks;
-    const int span_full = min(pb0e + a.part_blocks, a.max_blocks) - pb0e - wave;
+    const int pb0e = part * part_blocks;
+    const int span_full = min(pb0e + part_blocks, a.max_blocks) - pb0e - wave;
     const int nk_full = span_full > 0 ? (span_full + NW - 1) / NW : 0;
     if (lane < min(64, nk_full)) tb_first = trow[pb0e + wave + NW * lane];
   }
@@ -393,11 +410,10 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
 
   const Span sp = attended_span(a, seq);
   const int ctx = sp.ctx;
-  const int pb0 = sp.first_block + part * a.part_blocks;
-  if (pb0 >= sp.end_block && part != 0) return;  // partition past the context
-  const int pb1 = min(pb0 + a.part_blocks, sp.end_block);
-  const int nparts_seq = (sp.end_block - sp.first_block + a.part_blocks - 1) / a.part_blocks;
-  const bool direct = nparts_seq <= 1;
+  if (part >= sp.nparts && part != 0) return;  // partition past the context
+  const int pb0 = sp.origin / BS + part * part_blocks;
+  const int pb1 = min(pb0 + part_blocks, (ctx + BS - 1) / BS);
+  const bool direct = sp.nparts <= 1;
 
   SoftmaxState<G, E> st;
 #pragma unroll
@@ -409,7 +425,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   }
 
   const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * T::kRow;
-  const int64_t blk_stride = row_stride * kBlockSize;
+  const int64_t blk_stride = row_stride * BS;
   const int64_t lane_off = static_cast<int64_t>(kvh) * T::kRow + sub * 16 + rg * row_stride;
   const uint8_t* kbase = a.key_cache + lane_off;
   const uint8_t* vbase = a.value_cache + lane_off;
@@ -441,23 +457,23 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
         const int p = __builtin_amdgcn_readlane(tb, k + u);
         const int j = pb0 + wave + NW * (k0 + k + u);
         phys[u] = p < 0 ? 0 : p;
-        lo[u] = max(0, sp.first - j * kBlockSize);
-        valid[u] = p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize);
+        lo[u] = max(0, sp.first - j * BS);
+        valid[u] = p < 0 ? 0 : min(BS, ctx - j * BS);
         ks[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k + u));
         vs[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k + u));
       }
-      process_blocks<KF, QF, D, G, NW, UNROLL>(st, qf, kbase, vbase, blk_stride, row_stride, phys,
+      process_blocks<KF, QF, D, G, NW, BS, UNROLL>(st, qf, kbase, vbase, blk_stride, row_stride, phys,
                                                lo, valid, ks, vs, rg, a.scale_log2);
     }
     for (; k < kend; ++k) {
       const int p = __builtin_amdgcn_readlane(tb, k);
       const int j = pb0 + wave + NW * (k0 + k);
       int phys[1] = {p < 0 ? 0 : p};
-      int lo[1] = {max(0, sp.first - j * kBlockSize)};
-      int valid[1] = {p < 0 ? 0 : min(kBlockSize, ctx - j * kBlockSize)};
+      int lo[1] = {max(0, sp.first - j * BS)};
+      int valid[1] = {p < 0 ? 0 : min(BS, ctx - j * BS)};
       float ks[1] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k))};
       float vs[1] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k))};
-      process_blocks<KF, QF, D, G, NW, 1>(st, qf, kbase, vbase, blk_stride, row_stride, phys, lo,
+      process_blocks<KF, QF, D, G, NW, BS, 1>(st, qf, kbase, vbase, blk_stride, row_stride, phys, lo,
                                           valid, ks, vs, rg, a.scale_log2);
     }
   }
@@ -522,8 +538,7 @@ template <int QF, int D>
 __global__ void __launch_bounds__(D) paged_decode_reduce_kernel(DecodeArgs a) {
   const int sh = blockIdx.x;  // seq * num_heads + head
   const int seq = sh / a.num_heads;
-  const Span sp = attended_span(a, seq);
-  const int np = (sp.end_block - sp.first_block + a.part_blocks - 1) / a.part_blocks;
+  const int np = attended_span(a, seq).nparts;
   if (np <= 1) return;  // the decode kernel wrote this output directly
   const int d = threadIdx.x;
   const float* ml = a.ws_ml + static_cast<int64_t>(sh) * a.num_parts * 2;

@@ -25,7 +25,7 @@ def _sdpa(q, k, v, scale):
     return out[:, 0, :].numpy()
 
 
-def _contiguous_to_paged(k_list, v_list, fmt_dtype, rng, pool_extra=3, fill=np.nan):
+def _contiguous_to_paged(k_list, v_list, fmt_dtype, rng, pool_extra=3, fill=np.nan, bs=BS):
     """Scatter per-sequence contiguous K/V into a shuffled paged pool.
 
     Slots come from the allocator model appending one token at a time (the
@@ -33,21 +33,21 @@ def _contiguous_to_paged(k_list, v_list, fmt_dtype, rng, pool_extra=3, fill=np.n
     cache layout here does not reuse the decode oracle's address arithmetic.
     """
     hkv, d = k_list[0].shape[1], k_list[0].shape[2]
-    need = sum((len(k) + BS - 1) // BS for k in k_list)
+    need = sum((len(k) + bs - 1) // bs for k in k_list)
     nb = need + pool_extra
-    alloc = AllocatorModel(nb, BS)
+    alloc = AllocatorModel(nb, bs)
     alloc.set_free_order(rng.permutation(nb).tolist())
-    kc = np.full((nb, BS, hkv, d), fill, dtype=fmt_dtype)
-    vc = np.full((nb, BS, hkv, d), fill, dtype=fmt_dtype)
+    kc = np.full((nb, bs, hkv, d), fill, dtype=fmt_dtype)
+    vc = np.full((nb, bs, hkv, d), fill, dtype=fmt_dtype)
     sids = []
     for k, v in zip(k_list, v_list):
         sid = alloc.seq_create()
         sids.append(sid)
         slots, _ = alloc.seq_append_tokens(sid, len(k))
         for i, slot in enumerate(slots):
-            kc.reshape(nb * BS, hkv, d)[slot] = k[i]
-            vc.reshape(nb * BS, hkv, d)[slot] = v[i]
-    mb = max((len(k) + BS - 1) // BS for k in k_list) + 1
+            kc.reshape(nb * bs, hkv, d)[slot] = k[i]
+            vc.reshape(nb * bs, hkv, d)[slot] = v[i]
+    mb = max((len(k) + bs - 1) // bs for k in k_list) + 1
     tables, lens = alloc.export_block_tables(sids, mb, pad=-1)
     return kc, vc, np.array(tables, dtype=np.int32), np.array(lens, dtype=np.int32)
 
@@ -73,6 +73,27 @@ def pin_sdpa_contiguous(pa):
             v = np.repeat(v_list[s].astype(np.float32).astype(np.float64), g, axis=1)
             want = _sdpa(q32[s].astype(np.float64), k, v, scale)
             np.testing.assert_allclose(got[s], want, rtol=0, atol=1e-12)
+
+
+def pin_sdpa_other_block_sizes(pa):
+    """The same equality at block sizes 8, 32 and an odd 5 ([P1] deployment
+    section: the block size is a parameter), with a sliding window too."""
+    rng = np.random.default_rng(12)
+    h, hkv, d = 4, 2, 16
+    for bs in (8, 32, 5):
+        lens = [1, bs - 1, bs, bs + 1, 3 * bs + 2, 70]
+        k_list = [rng.standard_normal((n, hkv, d)).astype(np.float32) for n in lens]
+        v_list = [rng.standard_normal((n, hkv, d)).astype(np.float32) for n in lens]
+        q = rng.standard_normal((len(lens), h, d)).astype(np.float32)
+        kc, vc, tables, ctx = _contiguous_to_paged(k_list, v_list, np.float32, rng, bs=bs)
+        for window in (0, 9):
+            got = pa.paged_decode(q, "f32", kc, vc, "f32", tables, ctx, bs, 0.25, window=window)
+            for s, n in enumerate(lens):
+                lo = max(0, n - window) if window else 0
+                k = np.repeat(k_list[s][lo:].astype(np.float64), h // hkv, axis=1)
+                v = np.repeat(v_list[s][lo:].astype(np.float64), h // hkv, axis=1)
+                want = _sdpa(q[s].astype(np.float64), k, v, 0.25)
+                np.testing.assert_allclose(got[s], want, rtol=0, atol=1e-12)
 
 
 def pin_closed_forms(pa):
@@ -408,7 +429,7 @@ def pin_cache_write_fp8(pa):
 
 
 ALL_DECODE_PINS = [
-    pin_sdpa_contiguous, pin_closed_forms, pin_one_hot, pin_permutation_invariance,
+    pin_sdpa_contiguous, pin_sdpa_other_block_sizes, pin_closed_forms, pin_one_hot, pin_permutation_invariance,
     pin_shared_equals_duplicated, pin_gqa_equals_repeated_mha, pin_unread_slots_ignored,
     pin_int8_dequant, pin_fp8_dequant, pin_bf16_decode, pin_window_equals_contiguous_tail,
     pin_window_one_and_released_blocks,

@@ -102,6 +102,28 @@ def test_workspace_size_and_partition_policy():
     assert pkv.decode_workspace_size(2, 4, 3, 64, 16, 7) == 0          # 4 % 3 != 0
 
 
+def test_partition_policy_other_block_sizes():
+    """The policy is stated in tokens, so it picks the same partitions for the
+    same context whatever the block size; partitions are multiples of
+    max(block_size, 16) tokens and start at the window rounded down to that."""
+    for bs in (8, 16, 32):
+        mb = 2048 // bs
+        assert pkv.decode_partition_size(32, 64, 64, 128, bs, mb) == 0           # 2048 tokens whole
+        assert pkv.decode_partition_size(256, 32, 8, 128, bs, 4096 // bs) == 1024
+        assert pkv.decode_workspace_size(256, 32, 8, 128, bs, 4096 // bs) == 256 * 32 * 4 * 130 * 4
+        # few sequences: shrink until 512 workgroups (2 seqs x 2 kv heads -> 128 parts)
+        pt = pkv.decode_partition_size(2, 4, 2, 64, bs, 4096 // bs)
+        assert pt == 32 and pt % max(bs, 16) == 0
+    assert pkv.decode_partition_size(2, 4, 2, 64, 8, 7) == 16   # 56 tokens -> span 64, 4 parts of 16
+    assert pkv.decode_workspace_size(2, 4, 2, 64, 8, 7) == 2 * 4 * 4 * 66 * 4
+    assert pkv.decode_partition_size(2, 4, 4, 64, 8, 8, 8) == 0  # 8 tokens: not a multiple of 16
+    assert pkv.decode_partition_size(2, 4, 4, 64, 32, 8, 16) == 0
+    assert pkv.decode_partition_size(2, 4, 4, 64, 32, 8, 64) == 64
+    # a window of 4096 with 32-token blocks: span 4096 + 31 rounded up to 32 = 4128
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 32, 512, 0, 4096) == 32 * 32 * 5 * 130 * 4
+    assert pkv.decode_partition_size(2, 4, 4, 64, 12, 8) == 0   # block size not built
+
+
 def _decode(lib, **kw):
     args = dict(out=1, q=1, kc=1, vc=1, ks=None, vs=None, tables=1, lens=1, B=2, H=4, Hkv=4,
                 D=64, bs=16, MB=7, NB=32, scale=0.125, qf=pkv.F32, kvf=pkv.F32, part=0,
@@ -127,7 +149,11 @@ def _decode(lib, **kw):
     (dict(qf=pkv.BF16, kvf=pkv.FP8), pkv.ERR_INVALID_ARG),  # no scales
     (dict(qf=pkv.F16, kvf=5), pkv.ERR_INVALID_ARG),
     (dict(qf=7, kvf=7), pkv.ERR_INVALID_ARG),
-    (dict(bs=8), pkv.ERR_UNSUPPORTED),
+    (dict(bs=12), pkv.ERR_UNSUPPORTED),
+    (dict(bs=64), pkv.ERR_UNSUPPORTED),
+    (dict(bs=0), pkv.ERR_INVALID_ARG),
+    (dict(bs=8, part=8), pkv.ERR_INVALID_ARG),              # partitions are multiples of 16
+    (dict(bs=32, MB=4, part=16), pkv.ERR_INVALID_ARG),      # ... and of the block size
     (dict(D=96), pkv.ERR_UNSUPPORTED),
     (dict(H=12, Hkv=4), pkv.ERR_UNSUPPORTED),               # group of 3
     (dict(scale=float("nan")), pkv.ERR_INVALID_ARG),

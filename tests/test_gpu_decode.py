@@ -266,10 +266,11 @@ def _behind_window(wl, window):
     w2 = copy.copy(wl)
     w2.block_tables = wl.block_tables.copy()
     w2.key_cache, w2.value_cache = wl.key_cache.copy(), wl.value_cache.copy()
+    bs = wl.block_size
     for s, n in enumerate(wl.context_lens.tolist()):
         first = max(0, n - window)
         for i in range(first):
-            b, o = wl.block_tables[s, i // 16], i % 16
+            b, o = wl.block_tables[s, i // bs], i % bs
             for c in (w2.key_cache, w2.value_cache):
                 if wl.kv_fmt == "i8":
                     c[b, o] = np.int8(127)
@@ -279,7 +280,7 @@ def _behind_window(wl, window):
                     c[b, o] = np.uint16(0x7FC0)
                 else:
                     c[b, o] = np.nan
-        w2.block_tables[s, : first // 16] = -1
+        w2.block_tables[s, : first // bs] = -1
     return w2
 
 

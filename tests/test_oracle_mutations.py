@@ -10,6 +10,8 @@ import oracle_pins
 MUTATIONS = {
     "offset_uses_div": ("offset = tokens % block_size", "offset = tokens // block_size % block_size"),
     "block_uses_mod": ("logical_block = tokens // block_size", "logical_block = tokens % block_size"),
+    "block_size_fixed_16": ("logical_block = tokens // block_size", "logical_block = tokens // 16"),
+    "offset_fixed_16": ("offset = tokens % block_size", "offset = tokens % 16"),
     "dropped_scale": ("scores = scale * (k[:, kvh, :] @ qs[h])", "scores = (k[:, kvh, :] @ qs[h])"),
     "wrong_gqa_map": ("kvh = h // group", "kvh = h % num_kv_heads"),
     "no_max_shift_sign": ("w = np.exp(scores - m)", "w = np.exp(m - scores)"),
