@@ -489,7 +489,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-            "kernel": "paged_decode_kernel" + ("+reduce" if part else ""),
+            "kernel": ("paged_decode_kernel" if wl.kv_fmt == "f32" or wl.num_heads == wl.num_kv_heads
+                       else "paged_decode_gqa_kernel") + ("+paged_decode_reduce_kernel" if part else ""),
             "bytes_per_call": ab["total"], "decode_us": decode_us,
         },
         "decode_tokens_per_s": ctx_per_step / (decode_us * 1e-6),
