@@ -40,8 +40,9 @@ HBM_PEAK_GBPS = 8000.0
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "fp8": 1}
 SCALED = ("i8", "fp8")
 TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-3, "i8": 2e-2, "fp8": 2e-3}
-KERNEL_SOURCES = ["decode_kernel.h", "decode_dispatch.h", "decode.hip", "decode_f32.hip",
-                  "decode_f16.hip", "decode_bf16.hip", "decode_i8.hip", "decode_fp8.hip"]
+KERNEL_SOURCES = ["decode_kernel.h", "decode_gqa_kernel.h", "decode_prefix_kernel.h",
+                  "decode_dispatch.h", "decode.hip", "decode_f32.hip", "decode_f16.hip",
+                  "decode_bf16.hip", "decode_i8.hip", "decode_fp8.hip"]
 
 
 def kernel_hash():
@@ -340,6 +341,81 @@ def block_size_sweep(args, torch, pkv, W, log):
     print(json.dumps(result), flush=True)
 
 
+def shared_prefix_sweep(args, torch, pkv, W, log):
+    """The shared-prompt workload (64 sequences of 8 kv heads x 8 query heads,
+    bf16, a shared prefix plus 1..512 tokens each) at prefix lengths 2000,
+    8000, 16000 and 32000: decode sequence by sequence against the shared
+    prefix attended once for all sequences ([P2] Prefix Cache section).
+    HIP events around each call; both outputs checked against each other and
+    sampled sequences against the oracle.  Prints one JSON line."""
+    dev = torch.device("cuda:0")
+
+    def up(arr, fmt):
+        arr = np.ascontiguousarray(arr)
+        if fmt == "bf16":
+            return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(arr).to(dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+    rows = {}
+    for prefix in (2000, 8000, 16000, 32000):
+        mb = (prefix + 512) // 16 + 2
+        wl = W.make_workload(4, seed=args.seed, prefix=prefix,
+                             ctx=("prefix_plus_uniform", prefix, 1, 512), max_blocks=mb)
+        q, kc, vc = up(wl.q, wl.q_fmt), up(wl.key_cache, wl.kv_fmt), up(wl.value_cache, wl.kv_fmt)
+        tables, lens = up(wl.block_tables, "i32"), up(wl.context_lens, "i32")
+        B, H, D = q.shape
+        bs = wl.block_size
+        groups = [(0, B, wl.shared_prefix_blocks * bs)]
+        ws = torch.empty(max(pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, bs, mb), 1),
+                         dtype=torch.uint8, device=dev)
+        wsp = torch.empty(pkv.decode_prefix_workspace_size(B, H, wl.num_kv_heads, D, bs, mb, groups),
+                          dtype=torch.uint8, device=dev)
+        plens = torch.full((B,), groups[0][2], dtype=torch.int32, device=dev)
+        out, out2 = torch.empty_like(q), torch.empty_like(q)
+        per_seq = timed(lambda: pkv.paged_attention_decode(out, q, kc, vc, tables, lens, bs, wl.scale,
+                                                           workspace=ws))
+        shared = timed(lambda: pkv.paged_attention_decode_prefix(
+            out2, q, kc, vc, tables, lens, bs, wl.scale, groups, workspace=wsp, prefix_lens=plens))
+        err, seqs = parity_sample(wl, out2, n=2)
+        diff = float((out.float() - out2.float()).abs().max())
+        ab = algorithmic_bytes(wl)
+        rows[prefix] = {"per_sequence_us": per_seq, "shared_prefix_us": shared,
+                        "speedup": per_seq / shared, "unique_bytes": ab["total"],
+                        "logical_kv_bytes": ab["logical_kv"],
+                        "shared_prefix_unique_gbps": ab["total"] / (shared * 1e-6) / 1e9,
+                        "max_abs_diff_paths": diff, "parity_max_abs_err": err,
+                        "parity_seqs": seqs, "tol": TOL[wl.kv_fmt]}
+        log(f"prefix {prefix}: per-sequence {per_seq:.1f} us, shared prefix {shared:.1f} us "
+            f"({per_seq / shared:.2f}x), paths differ by {diff:.2g}, oracle err {err:.3g}")
+        del q, kc, vc, tables, lens, ws, wsp, out, out2
+    result = {
+        "metric": "decode of 64 sequences sharing a prompt: per-sequence against shared-prefix path",
+        "value": rows[32000]["speedup"], "unit": "x (per-sequence time / shared-prefix time, "
+                                                 "32000-token prefix)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": rows[32000]["shared_prefix_us"] / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "shared_prefix_gqa_bf16 at longer prefixes",
+                   "prefix_tokens": list(rows)},
+        "sweep": {str(k): v for k, v in rows.items()},
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +425,12 @@ def main():
                     help="workload 1..8 (default 3: 70B-shaped fp16; 6: sliding window; "
                          "7, 8: configurations 3 and 5 with an FP8 cache)")
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = library default)")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode a shared-prefix workload with the prefix attended once for all "
+                         "sequences (default: sequence by sequence, faster at a 2000-token prefix)")
+    ap.add_argument("--shared-prefix-sweep", action="store_true",
+                    help="measure both decode paths of the shared-prompt workload at prefix lengths "
+                         "2000 .. 32000 instead")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -384,6 +466,9 @@ def main():
     if args.block_size_sweep:
         block_size_sweep(args, torch, pkv, W, log)
         return
+    if args.shared_prefix_sweep:
+        shared_prefix_sweep(args, torch, pkv, W, log)
+        return
 
     t = time.perf_counter()
     wl = W.make_workload(args.config, seed=args.seed)
@@ -413,6 +498,13 @@ def main():
                                      wl.window)
     need = pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition,
                                      wl.window)
+    # --shared-prefix: a workload whose sequences share a prompt's blocks is
+    # decoded with the shared prefix attended once for the whole batch.
+    groups = prefix_lens = None
+    if wl.shared_prefix_blocks and not wl.window and args.shared_prefix:
+        groups = [(0, B, wl.shared_prefix_blocks * wl.block_size)]
+        need = pkv.decode_prefix_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, groups)
+        prefix_lens = torch.full((B,), groups[0][2], dtype=torch.int32, device=dev)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -420,8 +512,13 @@ def main():
         pkv.reshape_and_cache(k_new, v_new, kc, vc, slots, ks, vs)
 
     def decode():
-        pkv.paged_attention_decode(out, q, kc, vc, tables, lens, wl.block_size, wl.scale, ks, vs,
-                                   partition_size=args.partition, workspace=ws, window=wl.window)
+        if groups:
+            pkv.paged_attention_decode_prefix(out, q, kc, vc, tables, lens, wl.block_size, wl.scale,
+                                              groups, ks, vs, workspace=ws, prefix_lens=prefix_lens)
+        else:
+            pkv.paged_attention_decode(out, q, kc, vc, tables, lens, wl.block_size, wl.scale, ks,
+                                       vs, partition_size=args.partition, workspace=ws,
+                                       window=wl.window)
 
     for _ in range(args.warmup):
         write()
@@ -485,12 +582,16 @@ def main():
             "q_dtype": wl.q_fmt, "sum_context_tokens": ctx_per_step,
             "max_blocks_per_seq": MB, "num_blocks": wl.num_blocks,
             "partition_tokens": part, "seed": wl.seed, "sliding_window": wl.window,
+            "shared_prefix_tokens": groups[0][2] if groups else 0,
+            "decode_path": "shared-prefix" if groups else "per-sequence",
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-            "kernel": ("paged_decode_kernel" if wl.kv_fmt == "f32" or wl.num_heads == wl.num_kv_heads
-                       else "paged_decode_gqa_kernel") + ("+paged_decode_reduce_kernel" if part else ""),
+            "kernel": ("paged_prefix_kernel+" if groups else "") +
+                      ("paged_decode_kernel" if wl.kv_fmt == "f32" or wl.num_heads == wl.num_kv_heads
+                       else "paged_decode_gqa_kernel") +
+                      ("+paged_decode_reduce_kernel" if part or groups else ""),
             "bytes_per_call": ab["total"], "decode_us": decode_us,
         },
         "decode_tokens_per_s": ctx_per_step / (decode_us * 1e-6),

@@ -158,6 +158,50 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
                                int kv_dtype, int partition_size, int sliding_window,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Shared-prefix decode ([P1] "vLLM调度器与PagedAttention协同工作" item 2:
+ * requests that share a system prompt share its blocks; [P2] "Prefix Cache
+ * 复用共享前缀的KV Cache"): the same result as pkv_paged_attention_decode,
+ * computed so that a prefix shared by a group of sequences is attended once
+ * for all of the group's query heads instead of once per sequence.  A prefix
+ * kernel handles each group's shared tokens (many query rows per K/V tile, on
+ * the matrix cores), the decode kernels the rest of every context, and the
+ * merge kernel combines the two parts exactly.
+ *
+ * Groups are ranges of the batch:
+ *   groups        HOST int32 [3 * num_groups]: (first sequence, number of
+ *                 sequences, shared tokens) per group; the ranges lie within
+ *                 [0, num_seqs) and do not overlap (sequences outside every
+ *                 group have no shared prefix); shared tokens are a positive
+ *                 multiple of max(block_size, 16), at most
+ *                 max_blocks_per_seq * block_size
+ *   num_groups    1 .. 32
+ *   prefix_lens   device int32 [num_seqs]: the shared tokens of the
+ *                 sequence's group, 0 for a sequence outside every group
+ * Preconditions (not checked on the device): the sequences of a group have
+ * the same table entries for their shared tokens (as forks of a common
+ * prompt have) and context lengths >= the shared tokens.  Violations
+ * give wrong outputs but no out-of-bounds access.  No sliding window.
+ * workspace: >= pkv_decode_prefix_workspace_size(...) bytes (always needed).
+ * fp32 caches run the plain decode (no matrix-core path).
+ * Other arguments and errors as pkv_paged_attention_decode, plus INVALID_ARG
+ * for bad groups.
+ */
+int pkv_paged_attention_decode_prefix(void* out, const void* q, const void* key_cache,
+                                      const void* value_cache, const float* k_scales,
+                                      const float* v_scales, const int32_t* block_tables,
+                                      const int32_t* context_lens, const int32_t* prefix_lens,
+                                      int num_seqs, int num_heads, int num_kv_heads,
+                                      int head_dim, int block_size, int max_blocks_per_seq,
+                                      int num_blocks, float scale, int q_dtype, int kv_dtype,
+                                      const int32_t* groups, int num_groups, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+/* Workspace bytes of pkv_paged_attention_decode_prefix (0 for invalid shapes
+ * or groups). */
+size_t pkv_decode_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int max_blocks_per_seq,
+                                        const int32_t* groups, int num_groups);
+
 /* ------------------------------------------------------------------------ */
 /* Cache write                                                               */
 /* ------------------------------------------------------------------------ */

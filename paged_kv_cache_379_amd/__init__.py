@@ -16,6 +16,7 @@ import numpy as np
 __all__ = [
     "load", "LIB_PATH", "PkvError", "OutOfBlocks", "DoubleFree",
     "paged_attention_decode", "decode_workspace_size", "decode_partition_size",
+    "paged_attention_decode_prefix", "decode_prefix_workspace_size",
     "reshape_and_cache", "copy_blocks", "swap_blocks", "stream_copy", "validate_tables",
     "BlockAllocator", "F32", "F16", "BF16", "I8", "FP8", "SWAP_OUT", "SWAP_IN",
 ]
@@ -53,6 +54,9 @@ _SIGS = {
     "pkv_decode_workspace_size": (_c_size, [_c_int] * 8),
     "pkv_paged_attention_decode": (_c_int, [_vp] * 8 + [_c_int] * 7 + [ctypes.c_float] + [_c_int] * 4
                                    + [_vp, _c_size, _vp]),
+    "pkv_paged_attention_decode_prefix": (_c_int, [_vp] * 9 + [_c_int] * 7 + [ctypes.c_float]
+                                          + [_c_int] * 2 + [_i32p, _c_int, _vp, _c_size, _vp]),
+    "pkv_decode_prefix_workspace_size": (_c_size, [_c_int] * 6 + [_i32p, _c_int]),
     "pkv_reshape_and_cache": (_c_int, [_vp] * 7 + [_c_int] * 7 + [_vp]),
     "pkv_copy_blocks": (_c_int, [_vp] * 4 + [_i32p, _c_int, _c_size, _c_int, _c_int, _vp]),
     "pkv_swap_blocks": (_c_int, [_vp] * 8 + [_i32p, _c_int, _c_size] + [_c_int] * 4 + [_vp]),
@@ -213,6 +217,72 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
         _dev_ptr(context_lens, "context_lens", torch.int32),
         B, H, Hkv, D, bs, MB, NB, float(scale), _fmt(q), _fmt(key_cache), int(partition_size),
         int(window), _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(rc)
+    return out
+
+
+def _group_array(groups):
+    """[(first_seq, num_seqs, prefix_tokens), ...] -> host int32 [3 * G]."""
+    arr = np.ascontiguousarray(np.asarray(groups, dtype=np.int32).reshape(-1, 3))
+    if len(arr) == 0:
+        raise ValueError("at least one prefix group is needed")
+    return arr
+
+
+def decode_prefix_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                 max_blocks_per_seq, groups):
+    """Workspace bytes of :func:`paged_attention_decode_prefix`."""
+    arr = _group_array(groups)
+    return load().pkv_decode_prefix_workspace_size(
+        num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+        arr.ctypes.data_as(_i32p), len(arr))
+
+
+def paged_attention_decode_prefix(out, q, key_cache, value_cache, block_tables, context_lens,
+                                  block_size, scale, groups, k_scales=None, v_scales=None,
+                                  workspace=None, stream=None, prefix_lens=None):
+    """Decode with shared prefixes computed once per group (see include/pkv.h).
+
+    ``groups``: list of (first_seq, num_seqs, prefix_tokens): non-overlapping
+    ranges of the batch whose sequences share the blocks of their first
+    ``prefix_tokens`` tokens.  The result equals :func:`paged_attention_decode`.
+    ``prefix_lens`` (device int32 [B], each sequence's shared tokens) is built
+    from ``groups`` when not given.
+    """
+    torch = _torch()
+    lib = load()
+    B, H, D = q.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    if D2 != D or bs != block_size or tuple(out.shape) != (B, H, D) or out.dtype != q.dtype:
+        raise ValueError("shape or dtype mismatch between q, out and the caches")
+    if tuple(value_cache.shape) != tuple(key_cache.shape) or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    MB = block_tables.shape[1]
+    arr = _group_array(groups)
+    if prefix_lens is None:
+        lens = np.zeros(B, dtype=np.int32)
+        for first, n, p in arr.tolist():
+            lens[max(first, 0):max(first + n, 0)] = p
+        prefix_lens = torch.from_numpy(lens).to(q.device)
+    elif prefix_lens.shape != (B,):
+        raise ValueError("prefix_lens must be [B]")
+    need = lib.pkv_decode_prefix_workspace_size(B, H, Hkv, D, bs, MB, arr.ctypes.data_as(_i32p),
+                                                len(arr))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    rc = lib.pkv_paged_attention_decode_prefix(
+        _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(key_cache, "key_cache"),
+        _dev_ptr(value_cache, "value_cache"), _dev_ptr(k_scales, "k_scales", torch.float32),
+        _dev_ptr(v_scales, "v_scales", torch.float32),
+        _dev_ptr(block_tables, "block_tables", torch.int32),
+        _dev_ptr(context_lens, "context_lens", torch.int32),
+        _dev_ptr(prefix_lens, "prefix_lens", torch.int32),
+        B, H, Hkv, D, bs, MB, NB, float(scale), _fmt(q), _fmt(key_cache),
+        arr.ctypes.data_as(_i32p), len(arr), _dev_ptr(workspace, "workspace"), ws_bytes,
+        _stream(stream))
     _check(rc)
     return out
 

@@ -1,7 +1,9 @@
 // Host side of pkv_paged_attention_decode: argument checks, the partition
 // policy, the workspace contract and the two launches (decode, then the merge
 // of partitions when the context is split).
+#include <algorithm>
 #include <cmath>
+#include <vector>
 
 #include "decode_dispatch.h"
 #include "pkv_internal.h"
@@ -68,6 +70,108 @@ bool shapes_ok(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int 
          head_dim > 0 && block_size > 0 && max_blocks > 0;
 }
 
+// Checks shared by the decode entry points, for a non-empty batch whose
+// shapes passed shapes_ok.
+int check_decode(const void* out, const void* q, const void* key_cache, const void* value_cache,
+                 const float* k_scales, const float* v_scales, const int32_t* block_tables,
+                 const int32_t* context_lens, int num_heads, int num_kv_heads, int head_dim,
+                 int block_size, int max_blocks_per_seq, int kv_dtype, int q_dtype, float scale,
+                 int sliding_window) {
+  if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
+  const bool float_pair = (kv_dtype == PKV_F32 && q_dtype == PKV_F32) ||
+                          (kv_dtype == PKV_F16 && q_dtype == PKV_F16) ||
+                          (kv_dtype == PKV_BF16 && q_dtype == PKV_BF16);
+  const bool scaled_pair = (kv_dtype == PKV_I8 || kv_dtype == PKV_FP8) &&
+                           (q_dtype == PKV_F16 || q_dtype == PKV_BF16);
+  if (!float_pair && !scaled_pair)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "unsupported format pair q=%d kv=%d", q_dtype, kv_dtype);
+  if (scaled_pair && (!k_scales || !v_scales))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "int8 and fp8 caches need k_scales and v_scales");
+  if (head_dim != 64 && head_dim != 128)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", head_dim);
+  const int group = num_heads / num_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d (1, 2, 4, 8, 16)", group);
+  if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  if (sliding_window < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "sliding_window %d is negative", sliding_window);
+  if (!pkv_dev::supported_block_size(block_size))
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d (8, 16 or 32)", block_size);
+  // The kernels address one block's rows of a kv head with 32-bit offsets.
+  if (static_cast<int64_t>(num_kv_heads) * head_dim * pkv::elem_bytes(kv_dtype) * block_size >
+      INT32_MAX)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "a cache block is larger than 2 GiB");
+  return PKV_OK;
+}
+
+// Shared-prefix decode: prefix chunks of kMaxChunkTokens tokens, halved (down
+// to kMinChunkTokens) until the prefix kernel has kMinItems workgroups.
+constexpr int kMaxChunkTokens = 1024;  // at most 64 tiles: one table entry per lane
+constexpr int kMinChunkTokens = 128;
+
+struct PrefixPlan {
+  int chunk;        // tokens per prefix chunk
+  int max_chunks;   // chunks of the longest prefix: the slots before the rest's partitions
+  int parts;        // partitions of the rest of each context
+  int part_tokens;  // tokens per partition of the rest
+  int work_start[pkv_dev::kMaxPrefixGroups + 1];
+};
+
+int plan_prefix(int num_seqs, int num_heads, int num_kv_heads, int block_size, int max_blocks,
+                const int32_t* groups, int num_groups, PrefixPlan* plan) {
+  if (num_groups < 1 || num_groups > pkv_dev::kMaxPrefixGroups)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_groups %d (1 .. %d)", num_groups,
+                     pkv_dev::kMaxPrefixGroups);
+  if (!groups) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL groups");
+  const int u = pkv_dev::partition_align(block_size);
+  const int64_t cap = static_cast<int64_t>(max_blocks) * block_size;
+  std::vector<char> taken(num_seqs, 0);
+  for (int g = 0; g < num_groups; ++g) {
+    const int first = groups[3 * g], n = groups[3 * g + 1], prefix = groups[3 * g + 2];
+    if (first < 0 || n < 1 || static_cast<int64_t>(first) + n > num_seqs)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "group %d (%d, %d) outside the %d sequences", g, first,
+                       n, num_seqs);
+    for (int s = first; s < first + n; ++s) {
+      if (taken[s]) return pkv::fail(PKV_ERR_INVALID_ARG, "sequence %d is in two groups", s);
+      taken[s] = 1;
+    }
+    if (prefix <= 0 || prefix % u || prefix > cap)
+      return pkv::fail(PKV_ERR_INVALID_ARG, "group %d prefix %d must be a positive multiple of %d "
+                       "tokens, at most %lld", g, prefix, u, static_cast<long long>(cap));
+  }
+  const int G = num_heads / num_kv_heads;
+  auto work = [&](int chunk, int* starts) {
+    int64_t w = 0;
+    for (int g = 0; g < num_groups; ++g) {
+      if (starts) starts[g] = static_cast<int>(w);
+      const int64_t rows = static_cast<int64_t>(groups[3 * g + 1]) * G;
+      const int64_t tiles = (rows + 64 - 1) / 64;
+      w += static_cast<int64_t>(num_kv_heads) * tiles * ((groups[3 * g + 2] + chunk - 1) / chunk);
+    }
+    if (starts) starts[num_groups] = static_cast<int>(w);
+    return w;
+  };
+  int chunk = kMaxChunkTokens;
+  while (work(chunk, nullptr) < kMinItems && chunk / 2 >= kMinChunkTokens && (chunk / 2) % u == 0)
+    chunk /= 2;
+  if (chunk % u) chunk = u;  // 32-token blocks with 1024: stays a multiple
+  const int64_t total = work(chunk, plan->work_start);
+  if (total > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "prefix grid too large");
+  int max_chunks = 0;
+  for (int g = 0; g < num_groups; ++g)
+    max_chunks = std::max(max_chunks, (groups[3 * g + 2] + chunk - 1) / chunk);
+  const int64_t span = attended_tokens(max_blocks, block_size, 0);
+  const int64_t pt = partition_tokens(num_seqs, num_kv_heads, span, block_size, 0);
+  plan->chunk = chunk;
+  plan->max_chunks = max_chunks;
+  plan->part_tokens = static_cast<int>(pt);
+  plan->parts = static_cast<int>((span + pt - 1) / pt);
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,29 +220,11 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                      num_blocks);
   if (num_seqs == 0) return PKV_OK;
-  if (!out || !q || !key_cache || !value_cache || !block_tables || !context_lens)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL device pointer");
-  const bool float_pair = (kv_dtype == PKV_F32 && q_dtype == PKV_F32) ||
-                          (kv_dtype == PKV_F16 && q_dtype == PKV_F16) ||
-                          (kv_dtype == PKV_BF16 && q_dtype == PKV_BF16);
-  const bool scaled_pair = (kv_dtype == PKV_I8 || kv_dtype == PKV_FP8) &&
-                           (q_dtype == PKV_F16 || q_dtype == PKV_BF16);
-  if (!float_pair && !scaled_pair)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "unsupported format pair q=%d kv=%d", q_dtype, kv_dtype);
-  if (scaled_pair && (!k_scales || !v_scales))
-    return pkv::fail(PKV_ERR_INVALID_ARG, "int8 and fp8 caches need k_scales and v_scales");
-  if (head_dim != 64 && head_dim != 128)
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "head_dim %d (64 or 128)", head_dim);
+  if (int rc = check_decode(out, q, key_cache, value_cache, k_scales, v_scales, block_tables,
+                            context_lens, num_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, kv_dtype, q_dtype, scale, sliding_window))
+    return rc;
   const int group = num_heads / num_kv_heads;
-  if (group != 1 && group != 2 && group != 4 && group != 8 && group != 16)
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "query heads per kv head %d (1, 2, 4, 8, 16)", group);
-  if (!std::isfinite(scale)) return pkv::fail(PKV_ERR_INVALID_ARG, "scale is not finite");
-  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
-  if (sliding_window < 0)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "sliding_window %d is negative", sliding_window);
-  if (!pkv_dev::supported_block_size(block_size))
-    return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d (8, 16 or 32)", block_size);
   const int64_t span = attended_tokens(max_blocks_per_seq, block_size, sliding_window);
   const int64_t pt = partition_tokens(num_seqs, num_kv_heads, span, block_size, partition_size);
   if (pt <= 0)
@@ -151,10 +237,6 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   if (need > 0 && (!workspace || workspace_bytes < need))
     return pkv::fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
                      workspace_bytes, workspace ? "" : ", NULL");
-  // The kernels address one block's rows of a kv head with 32-bit offsets.
-  if (static_cast<int64_t>(num_kv_heads) * head_dim * pkv::elem_bytes(kv_dtype) * block_size >
-      INT32_MAX)
-    return pkv::fail(PKV_ERR_INVALID_ARG, "a cache block is larger than 2 GiB");
   const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * parts;
   if (items > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "grid too large");
 
@@ -182,6 +264,10 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   a.num_parts = parts;
   a.window = sliding_window;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.prefix_lens = nullptr;
+  a.part_base = 0;
+  a.prefix_chunk = 1;
+  a.merge_prefix = 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   bool ok = false;
@@ -202,6 +288,147 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
     const unsigned rgrid = static_cast<unsigned>(static_cast<int64_t>(num_seqs) * num_heads);
     switch (q_dtype) {
       case PKV_F32: err = pkv_dev::launch_reduce<PKV_F32>(head_dim, a, rgrid, s); break;
+      case PKV_F16: err = pkv_dev::launch_reduce<PKV_F16>(head_dim, a, rgrid, s); break;
+      default: err = pkv_dev::launch_reduce<PKV_BF16>(head_dim, a, rgrid, s); break;
+    }
+    if (err != hipSuccess)
+      return pkv::fail(PKV_ERR_HIP, "partition merge launch: %s", hipGetErrorString(err));
+  }
+  return PKV_OK;
+  PKV_API_END
+}
+
+size_t pkv_decode_prefix_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
+                                        int head_dim, int block_size, int max_blocks_per_seq,
+                                        const int32_t* groups, int num_groups) {
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
+      !pkv_dev::supported_block_size(block_size) ||
+      static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
+    return 0;
+  PrefixPlan plan;
+  if (plan_prefix(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq, groups,
+                  num_groups, &plan) != PKV_OK) {
+    pkv::clear_error();
+    return 0;
+  }
+  const size_t parts = static_cast<size_t>(plan.max_chunks) + plan.parts;
+  return static_cast<size_t>(num_seqs) * num_heads * parts * (head_dim + 2) * sizeof(float);
+}
+
+int pkv_paged_attention_decode_prefix(void* out, const void* q, const void* key_cache,
+                                      const void* value_cache, const float* k_scales,
+                                      const float* v_scales, const int32_t* block_tables,
+                                      const int32_t* context_lens, const int32_t* prefix_lens,
+                                      int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int max_blocks_per_seq, int num_blocks,
+                                      float scale, int q_dtype, int kv_dtype,
+                                      const int32_t* groups, int num_groups, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  PKV_API_BEGIN
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
+      num_blocks <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG,
+                     "bad shape: seqs=%d heads=%d kv_heads=%d head_dim=%d block_size=%d "
+                     "max_blocks=%d num_blocks=%d",
+                     num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                     num_blocks);
+  if (num_seqs == 0) return PKV_OK;
+  if (int rc = check_decode(out, q, key_cache, value_cache, k_scales, v_scales, block_tables,
+                            context_lens, num_heads, num_kv_heads, head_dim, block_size,
+                            max_blocks_per_seq, kv_dtype, q_dtype, scale, 0))
+    return rc;
+  if (!prefix_lens) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL prefix_lens");
+  PrefixPlan plan;
+  if (int rc = plan_prefix(num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                           groups, num_groups, &plan))
+    return rc;
+  // fp32 caches have no matrix-core path: the plain decode gives the same
+  // result (and needs no more workspace than the shared-prefix one).
+  if (kv_dtype == PKV_F32)
+    return pkv_paged_attention_decode(out, q, key_cache, value_cache, k_scales, v_scales,
+                                      block_tables, context_lens, num_seqs, num_heads,
+                                      num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                      num_blocks, scale, q_dtype, kv_dtype, 0, 0, workspace,
+                                      workspace_bytes, stream);
+  const int parts = plan.max_chunks + plan.parts;
+  const size_t need = static_cast<size_t>(num_seqs) * num_heads * parts * (head_dim + 2) *
+                      sizeof(float);
+  if (!workspace || workspace_bytes < need)
+    return pkv::fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
+                     workspace_bytes, workspace ? "" : ", NULL");
+  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * plan.parts;
+  if (items > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "grid too large");
+
+  pkv_dev::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.key_cache = static_cast<const uint8_t*>(key_cache);
+  a.value_cache = static_cast<const uint8_t*>(value_cache);
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  float* ws = static_cast<float*>(workspace);
+  const size_t slots = static_cast<size_t>(num_seqs) * num_heads * parts;
+  a.ws_ml = ws;
+  a.ws_acc = ws + 2 * slots;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.align = pkv_dev::partition_align(block_size);
+  a.part_tokens = plan.part_tokens;
+  a.num_parts = parts;
+  a.window = 0;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.prefix_lens = prefix_lens;
+  a.part_base = plan.max_chunks;
+  a.prefix_chunk = plan.chunk;
+  // With the rest of every context in one partition the decode kernel merges
+  // the prefix chunks into its own result; otherwise the merge kernel does.
+  a.merge_prefix = plan.parts == 1 ? 1 : 0;
+
+  pkv_dev::PrefixArgs pa;
+  pa.d = a;
+  pa.num_groups = num_groups;
+  for (int g = 0; g < num_groups; ++g) {
+    pa.group_first[g] = groups[3 * g];
+    pa.group_count[g] = groups[3 * g + 1];
+    pa.group_prefix[g] = groups[3 * g + 2];
+  }
+  for (int g = 0; g <= num_groups; ++g) pa.work_start[g] = plan.work_start[g];
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int group = num_heads / num_kv_heads;
+  bool ok = false;
+  hipError_t err = hipSuccess;
+  const unsigned pgrid = static_cast<unsigned>(plan.work_start[num_groups]);
+  switch (kv_dtype) {
+    case PKV_F16: err = pkv_dev::launch_prefix_f16(q_dtype, head_dim, pa, pgrid, s, ok); break;
+    case PKV_BF16: err = pkv_dev::launch_prefix_bf16(q_dtype, head_dim, pa, pgrid, s, ok); break;
+    case PKV_I8: err = pkv_dev::launch_prefix_i8(q_dtype, head_dim, pa, pgrid, s, ok); break;
+    case PKV_FP8: err = pkv_dev::launch_prefix_fp8(q_dtype, head_dim, pa, pgrid, s, ok); break;
+    default: break;
+  }
+  if (!ok) return pkv::fail(PKV_ERR_UNSUPPORTED, "no prefix kernel for this combination");
+  if (err != hipSuccess)
+    return pkv::fail(PKV_ERR_HIP, "prefix launch: %s", hipGetErrorString(err));
+  const unsigned grid = static_cast<unsigned>(items);
+  switch (kv_dtype) {
+    case PKV_F16: err = pkv_dev::launch_decode_f16(q_dtype, head_dim, group, a, grid, s, ok); break;
+    case PKV_BF16: err = pkv_dev::launch_decode_bf16(q_dtype, head_dim, group, a, grid, s, ok); break;
+    case PKV_I8: err = pkv_dev::launch_decode_i8(q_dtype, head_dim, group, a, grid, s, ok); break;
+    case PKV_FP8: err = pkv_dev::launch_decode_fp8(q_dtype, head_dim, group, a, grid, s, ok); break;
+    default: break;
+  }
+  if (!ok) return pkv::fail(PKV_ERR_UNSUPPORTED, "no kernel for this combination");
+  if (err != hipSuccess)
+    return pkv::fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
+  if (!a.merge_prefix) {
+    const unsigned rgrid = static_cast<unsigned>(static_cast<int64_t>(num_seqs) * num_heads);
+    switch (q_dtype) {
       case PKV_F16: err = pkv_dev::launch_reduce<PKV_F16>(head_dim, a, rgrid, s); break;
       default: err = pkv_dev::launch_reduce<PKV_BF16>(head_dim, a, rgrid, s); break;
     }

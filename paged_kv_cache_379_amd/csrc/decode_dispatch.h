@@ -7,6 +7,7 @@
 
 #include "decode_gqa_kernel.h"
 #include "decode_kernel.h"
+#include "decode_prefix_kernel.h"
 
 namespace pkv_dev {
 
@@ -77,6 +78,40 @@ hipError_t launch_decode_dims(int head_dim, int group, const DecodeArgs& a, unsi
   ok = false;
   return hipSuccess;
 }
+
+// The shared-prefix kernel (16-bit, int8 and fp8 caches; matrix cores).
+template <int KF, int QF, int D>
+hipError_t launch_prefix_block(int block_size, const PrefixArgs& pa, unsigned grid, hipStream_t s,
+                               bool& ok) {
+  ok = true;
+  const dim3 g(grid), b(kPrefixWaves * 64);
+  switch (block_size) {
+    case 8: hipLaunchKernelGGL((paged_prefix_kernel<KF, QF, D, 8>), g, b, 0, s, pa); break;
+    case 16: hipLaunchKernelGGL((paged_prefix_kernel<KF, QF, D, 16>), g, b, 0, s, pa); break;
+    case 32: hipLaunchKernelGGL((paged_prefix_kernel<KF, QF, D, 32>), g, b, 0, s, pa); break;
+    default: ok = false; return hipSuccess;
+  }
+  return hipGetLastError();
+}
+
+template <int KF, int QF>
+hipError_t launch_prefix_dims(int head_dim, const PrefixArgs& pa, unsigned grid, hipStream_t s,
+                              bool& ok) {
+  if (head_dim == 64) return launch_prefix_block<KF, QF, 64>(pa.d.block_size, pa, grid, s, ok);
+  if (head_dim == 128) return launch_prefix_block<KF, QF, 128>(pa.d.block_size, pa, grid, s, ok);
+  ok = false;
+  return hipSuccess;
+}
+
+// Defined in decode_f16.hip, decode_bf16.hip, decode_i8.hip, decode_fp8.hip.
+hipError_t launch_prefix_f16(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
+                             hipStream_t s, bool& ok);
+hipError_t launch_prefix_bf16(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
+                              hipStream_t s, bool& ok);
+hipError_t launch_prefix_i8(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
+                            hipStream_t s, bool& ok);
+hipError_t launch_prefix_fp8(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
+                             hipStream_t s, bool& ok);
 
 // Defined in decode_f32.hip, decode_f16.hip, decode_bf16.hip, decode_i8.hip,
 // decode_fp8.hip.

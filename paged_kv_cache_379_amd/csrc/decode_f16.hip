@@ -10,4 +10,11 @@ hipError_t launch_decode_f16(int q_dtype, int head_dim, int group, const DecodeA
   return hipSuccess;
 }
 
+hipError_t launch_prefix_f16(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
+                          hipStream_t s, bool& ok) {
+  if (q_dtype == PKV_F16) return launch_prefix_dims<PKV_F16, PKV_F16>(head_dim, pa, grid, s, ok);
+  ok = false;
+  return hipSuccess;
+}
+
 }  // namespace pkv_dev

@@ -398,9 +398,9 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
   // prologue waits for one memory round trip instead of three: this wave's
   // first table entries of the partition (as many as a full table holds;
   // entries past the context are never used), the query, and the length.
-  // With a sliding window the partitions start at the window, which depends
-  // on the length, so the table is read after it.
-  const bool early_table = a.window == 0;
+  // With a sliding window (or after a shared prefix) the partitions start at
+  // a token that depends on the length, so the table is read after it.
+  const bool early_table = a.window == 0 && !a.prefix_lens;
   const int max_tiles = (a.max_blocks * BS + kTileRows - 1) / kTileRows;
   int tb_first = -1, tb_first_b = -1;
   if (early_table) {
@@ -430,7 +430,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
   if (part >= sp.nparts && part != 0) return;  // partition past the context
   const int pt0 = sp.origin / kTileRows + part * part_tiles;
   const int pt1 = min(pt0 + part_tiles, (ctx + kTileRows - 1) / kTileRows);
-  const bool direct = sp.nparts <= 1;
+  const bool direct = sp.nparts <= 1 && !a.prefix_lens;
 
   GqaState<KF, QF, D> st;
   st.m = -INFINITY;
@@ -571,8 +571,10 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
     const int64_t sh = static_cast<int64_t>(seq) * a.num_heads + kvh * G + h;
     if (direct) {
       store_elem<QF>(a.out, sh * D + d, L > 0.f ? O / L : 0.f);
+    } else if (a.merge_prefix) {
+      store_merged_with_prefix<QF, D>(a, sh, d, Mx, L, O, sp.nchunks);
     } else {
-      const int64_t slot = sh * a.num_parts + part;
+      const int64_t slot = sh * a.num_parts + a.part_base + part;
       a.ws_acc[slot * D + d] = O;
       if (d == 0) {
         a.ws_ml[slot * 2] = Mx;

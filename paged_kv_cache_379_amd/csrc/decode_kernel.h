@@ -72,28 +72,48 @@ struct DecodeArgs {
   int num_parts;    // partitions per sequence in the grid
   int window;       // sliding window in tokens, 0 = the whole context
   float scale_log2; // scale * log2(e)
+  // Shared-prefix decode: the first prefix_lens[s] tokens of sequence s are
+  // attended by the prefix kernel, which writes its partials to the first
+  // part_base slots of each (sequence, head), prefix_chunk tokens per slot;
+  // the decode kernels then take the remaining tokens and always write
+  // partials, at slots part_base + p.  prefix_lens is NULL otherwise.
+  const int32_t* prefix_lens;
+  int part_base;
+  int prefix_chunk;
+  // Shared-prefix decode whose rest of every context is one partition: the
+  // decode kernel merges the prefix chunks itself and stores the output.
+  int merge_prefix;
 };
 
 // The attended part of a sequence's context: its length clamped to the table,
 // the first attended token (the last `window` tokens when a sliding window is
-// set), the origin of its partitions (the first token rounded down to the
-// partition alignment) and the number of partitions that hold tokens.
-// Partition p covers tokens origin + p * part_tokens onwards.
+// set; the first token after the shared prefix in shared-prefix decode), the
+// origin of its partitions (the first token rounded down to the partition
+// alignment), the number of partitions that hold tokens, and the number of
+// prefix-chunk partials written by the prefix kernel.  Partition p covers
+// tokens origin + p * part_tokens onwards.
 struct Span {
   int ctx;
   int first;
   int origin;
   int nparts;
+  int nchunks;
 };
 
 __device__ __forceinline__ Span attended_span(const DecodeArgs& a, int seq) {
   const int cap = a.max_blocks * a.block_size;
   int ctx = a.context_lens[seq];
   ctx = ctx < 0 ? 0 : (ctx > cap ? cap : ctx);
-  const int first = a.window > 0 ? max(0, ctx - a.window) : 0;
+  int first = a.window > 0 ? max(0, ctx - a.window) : 0;
+  int nchunks = 0;
+  if (a.prefix_lens) {
+    const int pl = min(max(a.prefix_lens[seq], 0), ctx);
+    first = max(first, pl);
+    nchunks = (pl + a.prefix_chunk - 1) / a.prefix_chunk;
+  }
   const int origin = first / a.align * a.align;
   const int nparts = ctx > origin ? (ctx - origin + a.part_tokens - 1) / a.part_tokens : 0;
-  return Span{ctx, first, origin, nparts};
+  return Span{ctx, first, origin, nparts, nchunks};
 }
 
 template <int F> struct Format;
@@ -356,6 +376,27 @@ __device__ __forceinline__ void process_blocks(
   }
 }
 
+// Store the output of (sequence, head) row sh from this workgroup's partial
+// (max m, sum l, accumulator o of dimension d, relative to m) merged with the
+// nchunks prefix-chunk partials in the workspace.
+template <int QF, int D>
+__device__ __forceinline__ void store_merged_with_prefix(const DecodeArgs& a, int64_t sh, int d,
+                                                         float m, float l, float o, int nchunks) {
+  const float* ml = a.ws_ml + sh * a.num_parts * 2;
+  const float* acc = a.ws_acc + sh * a.num_parts * D;
+  float M = m;
+  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, ml[2 * c]);
+  const float ms = (M == -INFINITY) ? 0.f : M;
+  const float f0 = fast_exp2(m - ms);
+  float L = l * f0, O = o * f0;
+  for (int c = 0; c < nchunks; ++c) {
+    const float f = fast_exp2(ml[2 * c] - ms);
+    L = fmaf(f, ml[2 * c + 1], L);
+    O = fmaf(f, acc[static_cast<int64_t>(c) * D + d], O);
+  }
+  store_elem<QF>(a.out, sh * D + d, L > 0.f ? O / L : 0.f);
+}
+
 template <int KF, int QF, int D, int G, int NW, int BS>
 __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   using T = DecodeTile<KF, QF, D, G, NW, BS>;
@@ -390,9 +431,9 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   // prologue waits for one memory round trip instead of three: this wave's
   // first table entries of the partition (as many as a full table holds;
   // entries past the context are never used), the query, and the length.
-  // With a sliding window the partitions start at the window, which depends
-  // on the length, so the table is read after it.
-  const bool early_table = a.window == 0;
+  // With a sliding window (or after a shared prefix) the partitions start at
+  // a token that depends on the length, so the table is read after it.
+  const bool early_table = a.window == 0 && !a.prefix_lens;
   int tb_first = -1;
   if (early_table) {
     const int pb0e = part * part_blocks;
@@ -413,7 +454,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   if (part >= sp.nparts && part != 0) return;  // partition past the context
   const int pb0 = sp.origin / BS + part * part_blocks;
   const int pb1 = min(pb0 + part_blocks, (ctx + BS - 1) / BS);
-  const bool direct = sp.nparts <= 1;
+  const bool direct = sp.nparts <= 1 && !a.prefix_lens;
 
   SoftmaxState<G, E> st;
 #pragma unroll
@@ -522,8 +563,10 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     const int64_t sh = static_cast<int64_t>(seq) * a.num_heads + h;
     if (direct) {
       store_elem<QF>(a.out, sh * D + d, L > 0.f ? O / L : 0.f);
+    } else if (a.merge_prefix) {
+      store_merged_with_prefix<QF, D>(a, sh, d, M, L, O, sp.nchunks);
     } else {
-      const int64_t slot = sh * a.num_parts + part;
+      const int64_t slot = sh * a.num_parts + a.part_base + part;
       a.ws_acc[slot * D + d] = O;
       if (d == 0) {
         a.ws_ml[slot * 2] = M;
@@ -538,16 +581,21 @@ template <int QF, int D>
 __global__ void __launch_bounds__(D) paged_decode_reduce_kernel(DecodeArgs a) {
   const int sh = blockIdx.x;  // seq * num_heads + head
   const int seq = sh / a.num_heads;
-  const int np = attended_span(a, seq).nparts;
-  if (np <= 1) return;  // the decode kernel wrote this output directly
+  const Span sp = attended_span(a, seq);
+  // The partials to merge: the prefix chunks (slots 0 .. nchunks - 1) and the
+  // partitions of the rest (slots part_base .. part_base + nparts - 1).
+  if (!a.prefix_lens && sp.nparts <= 1) return;  // the decode kernel wrote this output
   const int d = threadIdx.x;
   const float* ml = a.ws_ml + static_cast<int64_t>(sh) * a.num_parts * 2;
   const float* acc = a.ws_acc + static_cast<int64_t>(sh) * a.num_parts * D;
+  auto slot_of = [&](int i) { return i < sp.nchunks ? i : a.part_base + (i - sp.nchunks); };
+  const int n = sp.nchunks + sp.nparts;
   float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  for (int i = 0; i < n; ++i) M = fmaxf(M, ml[2 * slot_of(i)]);
   const float ms = (M == -INFINITY) ? 0.f : M;
   float L = 0.f, O = 0.f;
-  for (int p = 0; p < np; ++p) {
+  for (int i = 0; i < n; ++i) {
+    const int p = slot_of(i);
     const float f = fast_exp2(ml[2 * p] - ms);
     L = fmaf(f, ml[2 * p + 1], L);
     O = fmaf(f, acc[static_cast<int64_t>(p) * D + d], O);

@@ -235,3 +235,23 @@ def test_validate_tables():
     assert pkv.validate_tables(trimmed, [60], 16, 8, window=20) is None  # tokens 40..59
     assert pkv.validate_tables(trimmed, [60], 16, 8, window=30) == (0, 1)
     assert pkv.validate_tables(trimmed, [60], 16, 8) == (0, 0)
+
+
+def test_prefix_workspace_and_bad_groups():
+    """Shared-prefix decode: workspace from the chunk plan; invalid groups are
+    rejected on the host before anything is launched."""
+    # 64 forks of a 2000-token prompt, 8 kv heads of 8 query heads: 256-token
+    # chunks (8 of them), plus the whole rest of each context in one partition
+    assert pkv.decode_prefix_workspace_size(64, 64, 8, 128, 16, 157, [(0, 64, 2000)]) == \
+        64 * 64 * (8 + 1) * 130 * 4
+    assert pkv.decode_prefix_workspace_size(4, 4, 2, 64, 16, 8, [(0, 2, 24)]) == 0
+    assert pkv.decode_prefix_workspace_size(4, 4, 2, 64, 16, 8, [(0, 3, 16), (2, 2, 16)]) == 0
+    lib = pkv.load()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    for groups, n in (([0, 3, 16, 2, 2, 16], 2), ([3, 2, 16], 1), ([0, 2, 0], 1),
+                      ([0, 0, 16], 1), ([0, 1, 16], 0), ([0, 1, 16], 33)):
+        arr = np.array(groups, np.int32)
+        rc = lib.pkv_paged_attention_decode_prefix(
+            1, 1, 1, 1, None, None, 1, 1, 1, 4, 4, 2, 64, 16, 8, 32, 0.125, pkv.F16, pkv.F16,
+            arr.ctypes.data_as(i32p), n, 1, 1 << 20, None)
+        assert rc == pkv.ERR_INVALID_ARG, (groups, n)
