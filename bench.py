@@ -378,7 +378,8 @@ def shared_prefix_sweep(args, torch, pkv, W, log):
         tables, lens = up(wl.block_tables, "i32"), up(wl.context_lens, "i32")
         B, H, D = q.shape
         bs = wl.block_size
-        groups = [(0, B, wl.shared_prefix_blocks * bs)]
+        groups = pkv.find_shared_prefixes(wl.block_tables, wl.context_lens, bs)
+        assert groups == [(0, B, wl.shared_prefix_blocks * bs)], groups
         ws = torch.empty(max(pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, bs, mb), 1),
                          dtype=torch.uint8, device=dev)
         wsp = torch.empty(pkv.decode_prefix_workspace_size(B, H, wl.num_kv_heads, D, bs, mb, groups),
@@ -499,10 +500,13 @@ def main():
     need = pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition,
                                      wl.window)
     # --shared-prefix: a workload whose sequences share a prompt's blocks is
-    # decoded with the shared prefix attended once for the whole batch.
+    # decoded with the shared prefix attended once for the whole batch; the
+    # groups come from the host tables, as a scheduler would find them.
     groups = prefix_lens = None
     if wl.shared_prefix_blocks and not wl.window and args.shared_prefix:
-        groups = [(0, B, wl.shared_prefix_blocks * wl.block_size)]
+        groups = pkv.find_shared_prefixes(wl.block_tables, wl.context_lens, wl.block_size)
+        if len(groups) != 1:
+            raise SystemExit(f"expected one shared-prefix group, found {groups}")
         need = pkv.decode_prefix_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, groups)
         prefix_lens = torch.full((B,), groups[0][2], dtype=torch.int32, device=dev)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

@@ -424,6 +424,23 @@ int pkv_validate_tables(const int32_t* tables, const int32_t* lens, int num_seqs
                         int max_blocks, int block_size, int num_blocks,
                         int sliding_window, int* bad_seq, int* bad_block);
 
+/*
+ * Host helper for pkv_paged_attention_decode_prefix ([P1] scheduler section,
+ * item 2: forks of one prompt share its blocks): scans HOST copies of the
+ * tables in batch order and returns groups of consecutive sequences (at least
+ * max(min_group, 2) of them) whose tables hold the same block ids for their
+ * leading blocks.  A group's shared tokens are the whole blocks that every
+ * member's context covers and all members agree on, rounded down to
+ * max(block_size, 16), and at least min_tokens.  Greedy: a group grows while
+ * the next sequence keeps at least min_tokens shared.  At most 32 groups
+ * (the rest of the batch is then left ungrouped).  groups_out: host int32
+ * [3 * cap] receiving (first sequence, count, shared tokens); *n_groups their
+ * number (set also when cap is too small: INVALID_ARG).
+ */
+int pkv_find_shared_prefixes(const int32_t* tables, const int32_t* lens, int num_seqs,
+                             int max_blocks, int block_size, int min_tokens, int min_group,
+                             int32_t* groups_out, int cap, int* n_groups);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

@@ -16,7 +16,7 @@ import numpy as np
 __all__ = [
     "load", "LIB_PATH", "PkvError", "OutOfBlocks", "DoubleFree",
     "paged_attention_decode", "decode_workspace_size", "decode_partition_size",
-    "paged_attention_decode_prefix", "decode_prefix_workspace_size",
+    "paged_attention_decode_prefix", "decode_prefix_workspace_size", "find_shared_prefixes",
     "reshape_and_cache", "copy_blocks", "swap_blocks", "stream_copy", "validate_tables",
     "BlockAllocator", "F32", "F16", "BF16", "I8", "FP8", "SWAP_OUT", "SWAP_IN",
 ]
@@ -90,6 +90,8 @@ _SIGS = {
     "pkv_export_block_tables": (_c_int, [_vp, _i32p, _c_int, _c_int, ctypes.c_int32, _i32p, _i32p]),
     "pkv_validate_tables": (_c_int, [_i32p, _i32p, _c_int, _c_int, _c_int, _c_int, _c_int,
                                      ctypes.POINTER(_c_int), ctypes.POINTER(_c_int)]),
+    "pkv_find_shared_prefixes": (_c_int, [_i32p, _i32p] + [_c_int] * 5 + [_i32p, _c_int,
+                                                                         ctypes.POINTER(_c_int)]),
 }
 EXPORTED = tuple(_SIGS)
 SIGNATURES = _SIGS
@@ -391,6 +393,21 @@ def validate_tables(tables, lens, block_size, num_blocks, window=0):
     if rc == ERR_INVALID_ARG and bs_.value >= 0:
         return (bs_.value, bb.value)
     _check(rc)
+
+
+def find_shared_prefixes(tables, lens, block_size, min_tokens=256, min_group=2):
+    """Groups (first_seq, num_seqs, shared_tokens) of consecutive sequences
+    whose host tables share leading blocks (see include/pkv.h), ready for
+    :func:`paged_attention_decode_prefix`."""
+    lib = load()
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    l = np.ascontiguousarray(lens, dtype=np.int32)
+    out = np.empty(3 * 32, dtype=np.int32)
+    n = ctypes.c_int()
+    _check(lib.pkv_find_shared_prefixes(t.ctypes.data_as(_i32p), l.ctypes.data_as(_i32p),
+                                        t.shape[0], t.shape[1], block_size, min_tokens, min_group,
+                                        out.ctypes.data_as(_i32p), 32, ctypes.byref(n)))
+    return [tuple(int(x) for x in out[3 * i:3 * i + 3]) for i in range(n.value)]
 
 
 # ---------------------------------------------------------------------------

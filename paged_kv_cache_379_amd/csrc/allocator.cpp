@@ -551,4 +551,53 @@ int pkv_validate_tables(const int32_t* tables, const int32_t* lens, int num_seqs
   PKV_API_END
 }
 
+int pkv_find_shared_prefixes(const int32_t* tables, const int32_t* lens, int num_seqs,
+                             int max_blocks, int block_size, int min_tokens, int min_group,
+                             int32_t* groups_out, int cap, int* n_groups) {
+  PKV_API_BEGIN
+  if (num_seqs < 0 || max_blocks < 0 || block_size <= 0 || min_group < 1 || !n_groups ||
+      (num_seqs > 0 && (!tables || !lens)) || (cap > 0 && !groups_out))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "bad shape or NULL buffer");
+  const int64_t unit = block_size > 16 ? block_size : 16;  // shared tokens are multiples of this
+  const int64_t min_tok = std::max<int64_t>(min_tokens, unit);
+  // Whole blocks of sequence s that its context covers and that hold a valid id.
+  auto covered = [&](int s) {
+    const int64_t n = std::min<int64_t>(std::max(lens[s], 0), static_cast<int64_t>(max_blocks) * block_size);
+    return n / block_size;
+  };
+  auto entry = [&](int s, int64_t j) { return tables[static_cast<int64_t>(s) * max_blocks + j]; };
+  int found = 0;
+  int i = 0;
+  while (i < num_seqs && found < 32) {
+    int64_t common = covered(i);
+    int64_t k = 0;
+    while (k < common && entry(i, k) >= 0) ++k;
+    common = k;
+    int j = i + 1;
+    for (; j < num_seqs; ++j) {
+      int64_t c = std::min(common, covered(j));
+      int64_t m = 0;
+      while (m < c && entry(j, m) == entry(i, m)) ++m;
+      if (m * block_size / unit * unit < min_tok) break;
+      common = m;
+    }
+    const int64_t shared = common * block_size / unit * unit;
+    if (j - i >= min_group && j - i >= 2 && shared >= min_tok) {
+      if (found < cap) {
+        groups_out[3 * found] = i;
+        groups_out[3 * found + 1] = j - i;
+        groups_out[3 * found + 2] = static_cast<int32_t>(shared);
+      }
+      ++found;
+      i = j;
+    } else {
+      ++i;
+    }
+  }
+  *n_groups = found;
+  if (found > cap) return pkv::fail(PKV_ERR_INVALID_ARG, "capacity %d < %d groups", cap, found);
+  return PKV_OK;
+  PKV_API_END
+}
+
 }  // extern "C"

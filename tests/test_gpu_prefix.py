@@ -164,7 +164,8 @@ def test_prefix_shared_prompt_configuration_full_size(gpu_lib):
     pkv = gpu_lib
     wl = W.make_workload(4)
     dev = upload(wl)
-    groups = [(0, wl.num_seqs, wl.shared_prefix_blocks * wl.block_size)]
+    groups = pkv.find_shared_prefixes(wl.block_tables, wl.context_lens, wl.block_size)
+    assert groups == [(0, wl.num_seqs, wl.shared_prefix_blocks * wl.block_size)]
     out = torch.empty_like(dev["q"])
     pkv.paged_attention_decode_prefix(out, dev["q"], dev["key_cache"], dev["value_cache"],
                                       dev["block_tables"], dev["context_lens"], wl.block_size,
