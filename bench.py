@@ -341,6 +341,17 @@ def block_size_sweep(args, torch, pkv, W, log):
     print(json.dumps(result), flush=True)
 
 
+def decode_kernel_names(wl, part, shared_prefix):
+    """The kernels one decode call launches, joined by '+'."""
+    vector = wl.kv_fmt == "f32" or wl.num_heads == wl.num_kv_heads
+    if shared_prefix and wl.kv_fmt != "f32":
+        if vector:
+            return "paged_prefix_kernel+paged_decode_kernel+paged_decode_reduce_kernel"
+        return "paged_prefix_fused_kernel+paged_decode_reduce_kernel"
+    return ("paged_decode_kernel" if vector else "paged_decode_gqa_kernel") + \
+        ("+paged_decode_reduce_kernel" if part else "")
+
+
 def shared_prefix_sweep(args, torch, pkv, W, log):
     """The shared-prompt workload (64 sequences of 8 kv heads x 8 query heads,
     bf16, a shared prefix plus 1..512 tokens each) at prefix lengths 2000,
@@ -426,9 +437,9 @@ def main():
                     help="workload 1..8 (default 3: 70B-shaped fp16; 6: sliding window; "
                          "7, 8: configurations 3 and 5 with an FP8 cache)")
     ap.add_argument("--partition", type=int, default=0, help="tokens per partition (0 = library default)")
-    ap.add_argument("--shared-prefix", action="store_true",
-                    help="decode a shared-prefix workload with the prefix attended once for all "
-                         "sequences (default: sequence by sequence, faster at a 2000-token prefix)")
+    ap.add_argument("--per-sequence", action="store_true",
+                    help="decode a shared-prefix workload sequence by sequence (default: the shared "
+                         "prefix attended once for all sequences)")
     ap.add_argument("--shared-prefix-sweep", action="store_true",
                     help="measure both decode paths of the shared-prompt workload at prefix lengths "
                          "2000 .. 32000 instead")
@@ -499,11 +510,11 @@ def main():
                                      wl.window)
     need = pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, args.partition,
                                      wl.window)
-    # --shared-prefix: a workload whose sequences share a prompt's blocks is
-    # decoded with the shared prefix attended once for the whole batch; the
-    # groups come from the host tables, as a scheduler would find them.
+    # A workload whose sequences share a prompt's blocks is decoded with the
+    # shared prefix attended once for the whole batch (unless --per-sequence);
+    # the groups come from the host tables, as a scheduler would find them.
     groups = prefix_lens = None
-    if wl.shared_prefix_blocks and not wl.window and args.shared_prefix:
+    if wl.shared_prefix_blocks and not wl.window and not args.per_sequence:
         groups = pkv.find_shared_prefixes(wl.block_tables, wl.context_lens, wl.block_size)
         if len(groups) != 1:
             raise SystemExit(f"expected one shared-prefix group, found {groups}")
@@ -592,10 +603,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-            "kernel": ("paged_prefix_kernel+" if groups else "") +
-                      ("paged_decode_kernel" if wl.kv_fmt == "f32" or wl.num_heads == wl.num_kv_heads
-                       else "paged_decode_gqa_kernel") +
-                      ("+paged_decode_reduce_kernel" if part or groups else ""),
+            "kernel": decode_kernel_names(wl, part, bool(groups)),
             "bytes_per_call": ab["total"], "decode_us": decode_us,
         },
         "decode_tokens_per_s": ctx_per_step / (decode_us * 1e-6),

@@ -79,39 +79,58 @@ hipError_t launch_decode_dims(int head_dim, int group, const DecodeArgs& a, unsi
   return hipSuccess;
 }
 
-// The shared-prefix kernel (16-bit, int8 and fp8 caches; matrix cores).
-template <int KF, int QF, int D>
-hipError_t launch_prefix_block(int block_size, const PrefixArgs& pa, unsigned grid, hipStream_t s,
-                               bool& ok) {
+// The shared-prefix kernel (16-bit, int8 and fp8 caches; matrix cores):
+// n_prefix prefix work items alone (n_rest = 0), or together with the n_rest
+// grouped-query decode items of the rest of each context in one launch.
+template <int KF, int QF, int D, int BS>
+hipError_t launch_prefix_bs(int group, const PrefixArgs& pa, unsigned n_prefix, unsigned n_rest,
+                            hipStream_t s, bool& ok) {
   ok = true;
-  const dim3 g(grid), b(kPrefixWaves * 64);
-  switch (block_size) {
-    case 8: hipLaunchKernelGGL((paged_prefix_kernel<KF, QF, D, 8>), g, b, 0, s, pa); break;
-    case 16: hipLaunchKernelGGL((paged_prefix_kernel<KF, QF, D, 16>), g, b, 0, s, pa); break;
-    case 32: hipLaunchKernelGGL((paged_prefix_kernel<KF, QF, D, 32>), g, b, 0, s, pa); break;
-    default: ok = false; return hipSuccess;
+  const dim3 b(kPrefixWaves * 64);
+  if (n_rest == 0) {
+    hipLaunchKernelGGL((paged_prefix_kernel<KF, QF, D, BS>), dim3(n_prefix), b, 0, s, pa);
+  } else if (group >= 2 && group <= 8) {
+    hipLaunchKernelGGL((paged_prefix_fused_kernel<KF, QF, D, true, BS>), dim3(n_prefix + n_rest), b,
+                       0, s, pa, static_cast<int>(n_prefix));
+  } else if (group > 8 && group <= kMaxGroup) {
+    hipLaunchKernelGGL((paged_prefix_fused_kernel<KF, QF, D, false, BS>), dim3(n_prefix + n_rest),
+                       b, 0, s, pa, static_cast<int>(n_prefix));
+  } else {
+    ok = false;
+    return hipSuccess;
   }
   return hipGetLastError();
 }
 
+template <int KF, int QF, int D>
+hipError_t launch_prefix_block(int group, const PrefixArgs& pa, unsigned n_prefix,
+                               unsigned n_rest, hipStream_t s, bool& ok) {
+  switch (pa.d.block_size) {
+    case 8: return launch_prefix_bs<KF, QF, D, 8>(group, pa, n_prefix, n_rest, s, ok);
+    case 16: return launch_prefix_bs<KF, QF, D, 16>(group, pa, n_prefix, n_rest, s, ok);
+    case 32: return launch_prefix_bs<KF, QF, D, 32>(group, pa, n_prefix, n_rest, s, ok);
+    default: ok = false; return hipSuccess;
+  }
+}
+
 template <int KF, int QF>
-hipError_t launch_prefix_dims(int head_dim, const PrefixArgs& pa, unsigned grid, hipStream_t s,
-                              bool& ok) {
-  if (head_dim == 64) return launch_prefix_block<KF, QF, 64>(pa.d.block_size, pa, grid, s, ok);
-  if (head_dim == 128) return launch_prefix_block<KF, QF, 128>(pa.d.block_size, pa, grid, s, ok);
+hipError_t launch_prefix_dims(int head_dim, int group, const PrefixArgs& pa, unsigned n_prefix,
+                              unsigned n_rest, hipStream_t s, bool& ok) {
+  if (head_dim == 64) return launch_prefix_block<KF, QF, 64>(group, pa, n_prefix, n_rest, s, ok);
+  if (head_dim == 128) return launch_prefix_block<KF, QF, 128>(group, pa, n_prefix, n_rest, s, ok);
   ok = false;
   return hipSuccess;
 }
 
 // Defined in decode_f16.hip, decode_bf16.hip, decode_i8.hip, decode_fp8.hip.
-hipError_t launch_prefix_f16(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
-                             hipStream_t s, bool& ok);
-hipError_t launch_prefix_bf16(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
-                              hipStream_t s, bool& ok);
-hipError_t launch_prefix_i8(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
-                            hipStream_t s, bool& ok);
-hipError_t launch_prefix_fp8(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
-                             hipStream_t s, bool& ok);
+hipError_t launch_prefix_f16(int q_dtype, int head_dim, int group, const PrefixArgs& pa,
+                             unsigned n_prefix, unsigned n_rest, hipStream_t s, bool& ok);
+hipError_t launch_prefix_bf16(int q_dtype, int head_dim, int group, const PrefixArgs& pa,
+                              unsigned n_prefix, unsigned n_rest, hipStream_t s, bool& ok);
+hipError_t launch_prefix_i8(int q_dtype, int head_dim, int group, const PrefixArgs& pa,
+                            unsigned n_prefix, unsigned n_rest, hipStream_t s, bool& ok);
+hipError_t launch_prefix_fp8(int q_dtype, int head_dim, int group, const PrefixArgs& pa,
+                             unsigned n_prefix, unsigned n_rest, hipStream_t s, bool& ok);
 
 // Defined in decode_f32.hip, decode_f16.hip, decode_bf16.hip, decode_i8.hip,
 // decode_fp8.hip.

@@ -346,8 +346,23 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
   }
 }
 
+// LDS of one grouped-query workgroup: per-wave K/V tiles during the loop,
+// whose bytes then hold the waves' accumulators for the final merge, and the
+// waves' softmax states.
+template <int KF, int QF, int D, int NW>
+struct GqaShared {
+  static constexpr int kStageBytes = NW * 2 * GqaTile<KF, QF, D>::kTile;
+  static constexpr int kAccRow = D + 4;  // padded: the 16 columns' rows start in different banks
+  static constexpr int kMergeBytes = NW * 16 * kAccRow * 4;
+  static constexpr int kTileBytes = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
+  static constexpr int kBytes = kTileBytes + 2 * NW * 16 * 4;
+};
+
+// Work item `item` of the grouped-query decode (one kv head of one sequence
+// and partition), with `smem` the workgroup's GqaShared bytes (16-byte
+// aligned).  Every thread of the workgroup calls it.
 template <int KF, int QF, int D, int NW, bool SPLIT, int BS>
-__global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a) {
+__device__ __forceinline__ void gqa_decode_body(const DecodeArgs& a, int item, uint8_t* smem) {
   using T = GqaTile<KF, QF, D>;
   constexpr bool kTwo = BS < kTileRows;                     // two blocks per tile
   constexpr int kTilesPerBlock = BS > kTileRows ? BS / kTileRows : 1;
@@ -365,15 +380,11 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
     }
   };
 
-  // Per-wave K/V tiles during the loop; the same bytes then hold the waves'
-  // accumulators for the final merge.
-  constexpr int kStageBytes = NW * 2 * T::kTile;
-  constexpr int kAccRow = D + 4;  // padded: the 16 columns' rows start in different banks
-  constexpr int kMergeBytes = NW * 16 * kAccRow * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes];
-  __shared__ float s_m[NW][16];
-  __shared__ float s_l[NW][16];
+  using Lds = GqaShared<KF, QF, D, NW>;
+  constexpr int kAccRow = Lds::kAccRow;
   float (*s_acc)[16][kAccRow] = reinterpret_cast<float (*)[16][kAccRow]>(smem);
+  float (*s_m)[16] = reinterpret_cast<float (*)[16]>(smem + Lds::kTileBytes);
+  float (*s_l)[16] = s_m + NW;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -385,7 +396,6 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
   // each XCD sees every partition index and the same kv heads of every
   // sequence (shared prefix blocks of a kv head then meet in one L2), and
   // partitions past short contexts sit at the tail of the grid.
-  const int item = blockIdx.x;
   const int nsk = a.num_seqs * a.num_kv_heads;
   const int part = item / nsk;
   const int sk = item - part * nsk;
@@ -582,6 +592,12 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a)
       }
     }
   }
+}
+
+template <int KF, int QF, int D, int NW, bool SPLIT, int BS>
+__global__ void __launch_bounds__(NW * 64) paged_decode_gqa_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[GqaShared<KF, QF, D, NW>::kBytes];
+  gqa_decode_body<KF, QF, D, NW, SPLIT, BS>(a, blockIdx.x, smem);
 }
 
 }  // namespace pkv_dev

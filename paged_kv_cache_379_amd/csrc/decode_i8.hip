@@ -12,10 +12,12 @@ hipError_t launch_decode_i8(int q_dtype, int head_dim, int group, const DecodeAr
   return hipSuccess;
 }
 
-hipError_t launch_prefix_i8(int q_dtype, int head_dim, const PrefixArgs& pa, unsigned grid,
-                          hipStream_t s, bool& ok) {
-  if (q_dtype == PKV_F16) return launch_prefix_dims<PKV_I8, PKV_F16>(head_dim, pa, grid, s, ok);
-  if (q_dtype == PKV_BF16) return launch_prefix_dims<PKV_I8, PKV_BF16>(head_dim, pa, grid, s, ok);
+hipError_t launch_prefix_i8(int q_dtype, int head_dim, int group, const PrefixArgs& pa,
+                            unsigned n_prefix, unsigned n_rest, hipStream_t s, bool& ok) {
+  if (q_dtype == PKV_F16)
+    return launch_prefix_dims<PKV_I8, PKV_F16>(head_dim, group, pa, n_prefix, n_rest, s, ok);
+  if (q_dtype == PKV_BF16)
+    return launch_prefix_dims<PKV_I8, PKV_BF16>(head_dim, group, pa, n_prefix, n_rest, s, ok);
   ok = false;
   return hipSuccess;
 }

@@ -11,7 +11,8 @@
 // kernel's tile step (scores, online softmax, weighted V sum) on it with its
 // own 16 rows.  The partial (max, sum, accumulator) of each row goes to the
 // workspace slot of its chunk; the merge kernel combines the chunks with the
-// partials of the rest of each context, which the decode kernels compute.
+// partials of the rest of each context, which the decode kernels compute (for
+// grouped-query heads in the same launch, after the prefix items).
 #pragma once
 
 #include "decode_gqa_kernel.h"
@@ -30,8 +31,17 @@ struct PrefixArgs {
   int work_start[kMaxPrefixGroups + 1];   // first workgroup of each group
 };
 
+// LDS of one prefix workgroup: two buffers of a K tile and a V tile.
+template <int KF, int QF, int D>
+struct PrefixShared {
+  static constexpr int kBytes = 2 * 2 * GqaTile<KF, QF, D>::kTile;
+};
+
+// Prefix work item `item` (group, kv head, row tile, chunk), with `smem` the
+// workgroup's PrefixShared bytes (16-byte aligned).  Every thread of the
+// workgroup calls it.
 template <int KF, int QF, int D, int BS>
-__global__ void __launch_bounds__(kPrefixWaves * 64) paged_prefix_kernel(PrefixArgs pa) {
+__device__ __forceinline__ void prefix_body(const PrefixArgs& pa, int item, uint8_t* smem) {
   using T = GqaTile<KF, QF, D>;
   constexpr int NW = kPrefixWaves;
   constexpr bool kTwo = BS < kTileRows;
@@ -41,7 +51,6 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) paged_prefix_kernel(PrefixA
   static_assert(kLoadLanes <= 64, "a quarter tile per wave in one load");
   const DecodeArgs& a = pa.d;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * T::kTile];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -51,7 +60,6 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) paged_prefix_kernel(PrefixA
   // Group, then (kv head fastest: workgroup i runs on XCD i % 8, so with
   // num_kv_heads a multiple of 8 each kv head's prefix stays in one L2),
   // row tile and chunk.
-  const int item = blockIdx.x;
   int grp = 0;
   while (grp + 1 < pa.num_groups && item >= pa.work_start[grp + 1]) ++grp;
   const int local = item - pa.work_start[grp];
@@ -230,6 +238,33 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) paged_prefix_kernel(PrefixA
       a.ws_ml[slot * 2 + 1] = st.l;
     }
   }
+}
+
+template <int KF, int QF, int D, int BS>
+__global__ void __launch_bounds__(kPrefixWaves * 64) paged_prefix_kernel(PrefixArgs pa) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PrefixShared<KF, QF, D>::kBytes];
+  prefix_body<KF, QF, D, BS>(pa, blockIdx.x, smem);
+}
+
+// Shared-prefix decode in one launch (grouped-query heads): the n_prefix
+// prefix work items first, then the n_rest decode items of the rest of each
+// context (pa.d, which writes partials for the merge kernel).  The rest items
+// fill the CUs as the prefix items drain, so the tail of the compute-bound
+// prefix work overlaps the memory-bound rest instead of waiting for a second
+// launch.  (Dealing the two kinds in alternating runs measured slower at long
+// prefixes: the rest items then compete with every prefix chunk.)
+template <int KF, int QF, int D, bool SPLIT, int BS>
+__global__ void __launch_bounds__(kPrefixWaves * 64)
+    paged_prefix_fused_kernel(PrefixArgs pa, int n_prefix) {
+  static_assert(kPrefixWaves == 4, "both kinds run on four waves");
+  constexpr int kP = PrefixShared<KF, QF, D>::kBytes;
+  constexpr int kR = GqaShared<KF, QF, D, 4>::kBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kP > kR ? kP : kR];
+  const int i = blockIdx.x;
+  if (i < n_prefix)
+    prefix_body<KF, QF, D, BS>(pa, i, smem);
+  else
+    gqa_decode_body<KF, QF, D, 4, SPLIT, BS>(pa.d, i - n_prefix, smem);
 }
 
 }  // namespace pkv_dev

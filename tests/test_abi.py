@@ -240,10 +240,11 @@ def test_validate_tables():
 def test_prefix_workspace_and_bad_groups():
     """Shared-prefix decode: workspace from the chunk plan; invalid groups are
     rejected on the host before anything is launched."""
-    # 64 forks of a 2000-token prompt, 8 kv heads of 8 query heads: 256-token
-    # chunks (8 of them), plus the whole rest of each context in one partition
+    # 64 forks of a 2000-token prompt, 8 kv heads of 8 query heads: 512-token
+    # chunks (4 of them: 8 kv heads x 8 row tiles x 4 = 256 prefix workgroups),
+    # plus the whole rest of each context in one partition
     assert pkv.decode_prefix_workspace_size(64, 64, 8, 128, 16, 157, [(0, 64, 2000)]) == \
-        64 * 64 * (8 + 1) * 130 * 4
+        64 * 64 * (4 + 1) * 130 * 4
     assert pkv.decode_prefix_workspace_size(4, 4, 2, 64, 16, 8, [(0, 2, 24)]) == 0
     assert pkv.decode_prefix_workspace_size(4, 4, 2, 64, 16, 8, [(0, 3, 16), (2, 2, 16)]) == 0
     lib = pkv.load()

@@ -147,9 +147,11 @@ def test_prefix_rejects_bad_groups(gpu_lib):
 
 
 def test_prefix_merged_in_the_decode_kernel(gpu_lib):
-    """512 (sequence, kv head) pairs and short contexts: the rest of every
-    context is one partition, so the decode kernel merges the prefix chunks
-    itself (no merge kernel)."""
+    """512 (sequence, kv head) pairs and short contexts, so the rest of every
+    context is one partition.  With one query head per kv head (the second
+    batch) the multi-head decode kernel then merges the prefix chunks itself,
+    with no merge kernel; with two (the first) the prefix and the rest share
+    one launch and the merge kernel combines them."""
     rng = np.random.default_rng(21)
     _run(gpu_lib, rng, "f16", "f16", 2, 8, 64, 16, [(64, 40), (0, 12), (96, 12)])
     rng = np.random.default_rng(22)
