@@ -177,3 +177,38 @@ def test_prefix_shared_prompt_configuration_full_size(gpu_lib):
     seqs = np.array([0, 17, 40, 63])
     assert_parity(got[seqs], oracle_decode(wl, seqs), "bf16", label="shared prompt full size")
     assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("prefix", [8000, 16000])
+def test_prefix_long_shared_prompts(gpu_lib, prefix):
+    """64 forks of an 8000- or 16000-token prompt: 1024-token chunks (the
+    largest; 512 and 1024 prefix workgroups) with a partial last chunk, in
+    one launch with the rest of each context.  Sampled sequences against the
+    oracle, and the result equals the per-sequence decode."""
+    from gpu_util import oracle_decode, upload
+    from paged_kv_cache_379_amd import workloads as W
+    pkv = gpu_lib
+    mb = (prefix + 512) // 16 + 2
+    wl = W.make_workload(4, prefix=prefix, ctx=("prefix_plus_uniform", prefix, 1, 512),
+                         max_blocks=mb)
+    dev = upload(wl)
+    groups = pkv.find_shared_prefixes(wl.block_tables, wl.context_lens, wl.block_size)
+    assert groups == [(0, 64, prefix)]
+    B, H, D = dev["q"].shape
+    ws_size = pkv.decode_prefix_workspace_size(B, H, wl.num_kv_heads, D, 16, mb, groups)
+    chunk = 1024
+    rest_parts = (mb * 16 + 1023) // 1024
+    assert ws_size == B * H * (-(-prefix // chunk) + rest_parts) * (D + 2) * 4
+    out = torch.empty_like(dev["q"])
+    pkv.paged_attention_decode_prefix(out, dev["q"], dev["key_cache"], dev["value_cache"],
+                                      dev["block_tables"], dev["context_lens"], 16, wl.scale,
+                                      groups)
+    plain = torch.empty_like(out)
+    pkv.paged_attention_decode(plain, dev["q"], dev["key_cache"], dev["value_cache"],
+                               dev["block_tables"], dev["context_lens"], 16, wl.scale)
+    torch.cuda.synchronize()
+    got = out_f64(out)
+    seqs = np.array([3, 38, 61])
+    assert_parity(got[seqs], oracle_decode(wl, seqs), "bf16", label=f"prefix {prefix}")
+    assert np.isfinite(got).all()
+    assert (out.float() - plain.float()).abs().max().item() < 4e-3
