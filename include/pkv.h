@@ -165,8 +165,10 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
  * computed so that a prefix shared by a group of sequences is attended once
  * for all of the group's query heads instead of once per sequence.  A prefix
  * kernel handles each group's shared tokens (many query rows per K/V tile, on
- * the matrix cores), the decode kernels the rest of every context, and the
- * merge kernel combines the two parts exactly.
+ * the matrix cores), the decode kernels the rest of every context (for
+ * grouped-query heads in the same launch, after the prefix work), and the two
+ * parts are combined exactly.  No host synchronisation or allocation: the
+ * call can be captured in a HIP graph.
  *
  * Groups are ranges of the batch:
  *   groups        HOST int32 [3 * num_groups]: (first sequence, number of

@@ -581,9 +581,7 @@ __device__ __forceinline__ void gqa_decode_body(const DecodeArgs& a, int item, u
     const int64_t sh = static_cast<int64_t>(seq) * a.num_heads + kvh * G + h;
     if (direct) {
       store_elem<QF>(a.out, sh * D + d, L > 0.f ? O / L : 0.f);
-    } else if (a.merge_prefix) {
-      store_merged_with_prefix<QF, D>(a, sh, d, Mx, L, O, sp.nchunks);
-    } else {
+    } else {  // a partition's (or, after a shared prefix, the rest's) partial
       const int64_t slot = sh * a.num_parts + a.part_base + part;
       a.ws_acc[slot * D + d] = O;
       if (d == 0) {

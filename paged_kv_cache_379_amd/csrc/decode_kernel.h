@@ -80,8 +80,9 @@ struct DecodeArgs {
   const int32_t* prefix_lens;
   int part_base;
   int prefix_chunk;
-  // Shared-prefix decode whose rest of every context is one partition: the
-  // decode kernel merges the prefix chunks itself and stores the output.
+  // Shared-prefix decode with one query head per kv head whose rest of every
+  // context is one partition: the multi-head decode kernel merges the prefix
+  // chunks itself and stores the output.
   int merge_prefix;
 };
 
