@@ -148,8 +148,12 @@ def _torch():
 
 def _fmt(t):
     torch = _torch()
-    return {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
-            torch.float8_e4m3fn: FP8}[t.dtype]
+    fmt = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16, torch.int8: I8,
+           torch.float8_e4m3fn: FP8}.get(t.dtype)
+    if fmt is None:
+        raise ValueError(f"unsupported dtype {t.dtype} (float32, float16, bfloat16, int8, "
+                         "float8_e4m3fn)")
+    return fmt
 
 
 def _dev_ptr(t, name, dtype=None):

@@ -256,3 +256,12 @@ def test_prefix_workspace_and_bad_groups():
             1, 1, 1, 1, None, None, 1, 1, 1, 4, 4, 2, 64, 16, 8, 32, 0.125, pkv.F16, pkv.F16,
             arr.ctypes.data_as(i32p), n, 1, 1 << 20, None)
         assert rc == pkv.ERR_INVALID_ARG, (groups, n)
+
+
+def test_binding_rejects_unsupported_dtypes():
+    import torch
+    with pytest.raises(ValueError, match="unsupported dtype"):
+        pkv._fmt(torch.zeros(1, dtype=torch.float64))
+    for dt, want in ((torch.float16, pkv.F16), (torch.bfloat16, pkv.BF16), (torch.int8, pkv.I8),
+                     (torch.float8_e4m3fn, pkv.FP8), (torch.float32, pkv.F32)):
+        assert pkv._fmt(torch.zeros(1, dtype=dt)) == want
