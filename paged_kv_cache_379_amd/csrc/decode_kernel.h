@@ -71,6 +71,7 @@ struct DecodeArgs {
   int part_tokens;  // tokens per partition, a multiple of align
   int num_parts;    // partitions per sequence in the grid
   int window;       // sliding window in tokens, 0 = the whole context
+  int heads_per_item;  // multi-head kernel: kv heads per workgroup (1, 2 or 4)
   float scale_log2; // scale * log2(e)
   // Shared-prefix decode: the first prefix_lens[s] tokens of sequence s are
   // attended by the prefix kernel, which writes its partials to the first
@@ -420,12 +421,25 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   // each XCD sees every partition index and the same kv heads of every
   // sequence (shared prefix blocks of a kv head then meet in one L2), and
   // partitions past short contexts sit at the tail of the grid.
+  //
+  // A workgroup serves hpw neighbouring kv heads of one sequence and
+  // partition: wave w takes kv head w % hpw and every (NW / hpw)-th block of
+  // the partition from block w / hpw.  The heads' rows of a block are
+  // adjacent in the cache, so one CU then reads hpw x head_dim x element
+  // bytes of each token row at about the same time instead of one head's
+  // 128 or 256 bytes.
+  const int hpw = a.heads_per_item;
+  const int wph = NW / hpw;
+  const int hsub = wave % hpw;
+  const int wslot = wave / hpw;
   const int item = blockIdx.x;
-  const int nsk = a.num_seqs * a.num_kv_heads;
+  const int gps = a.num_kv_heads / hpw;
+  const int nsk = a.num_seqs * gps;
   const int part = item / nsk;
   const int sk = item - part * nsk;
-  const int kvh = sk % a.num_kv_heads;
-  const int seq = sk / a.num_kv_heads;
+  const int seq = sk / gps;
+  const int kvh0 = (sk - seq * gps) * hpw;
+  const int kvh = kvh0 + hsub;
 
   const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
   // Issued together, before the context length is known, so that the
@@ -438,9 +452,9 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   int tb_first = -1;
   if (early_table) {
     const int pb0e = part * part_blocks;
-    const int span_full = min(pb0e + part_blocks, a.max_blocks) - pb0e - wave;
-    const int nk_full = span_full > 0 ? (span_full + NW - 1) / NW : 0;
-    if (lane < min(64, nk_full)) tb_first = trow[pb0e + wave + NW * lane];
+    const int span_full = min(pb0e + part_blocks, a.max_blocks) - pb0e - wslot;
+    const int nk_full = span_full > 0 ? (span_full + wph - 1) / wph : 0;
+    if (lane < min(64, nk_full)) tb_first = trow[pb0e + wslot + wph * lane];
   }
 
   float qf[G][E];
@@ -472,15 +486,15 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   const uint8_t* kbase = a.key_cache + lane_off;
   const uint8_t* vbase = a.value_cache + lane_off;
 
-  // Blocks of this wave: pb0 + wave + NW * k for k < nk.
-  const int span = pb1 - pb0 - wave;
-  const int nk = span > 0 ? (span + NW - 1) / NW : 0;
+  // Blocks of this wave: pb0 + wslot + wph * k for k < nk.
+  const int span = pb1 - pb0 - wslot;
+  const int nk = span > 0 ? (span + wph - 1) / wph : 0;
   for (int k0 = 0; k0 < nk; k0 += 64) {
     const int kk = k0 + lane;
     int tb = -1;
     float tks = 1.f, tvs = 1.f;
     if (kk < nk) {
-      tb = (k0 == 0 && early_table) ? tb_first : trow[pb0 + wave + NW * kk];
+      tb = (k0 == 0 && early_table) ? tb_first : trow[pb0 + wslot + wph * kk];
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
       if constexpr (scaled_format(KF)) {
         if (tb >= 0) {
@@ -497,7 +511,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const int p = __builtin_amdgcn_readlane(tb, k + u);
-        const int j = pb0 + wave + NW * (k0 + k + u);
+        const int j = pb0 + wslot + wph * (k0 + k + u);
         phys[u] = p < 0 ? 0 : p;
         lo[u] = max(0, sp.first - j * BS);
         valid[u] = p < 0 ? 0 : min(BS, ctx - j * BS);
@@ -509,7 +523,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     }
     for (; k < kend; ++k) {
       const int p = __builtin_amdgcn_readlane(tb, k);
-      const int j = pb0 + wave + NW * (k0 + k);
+      const int j = pb0 + wslot + wph * (k0 + k);
       int phys[1] = {p < 0 ? 0 : p};
       int lo[1] = {max(0, sp.first - j * BS)};
       int valid[1] = {p < 0 ? 0 : min(BS, ctx - j * BS)};
@@ -545,22 +559,22 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // Merge the waves and write the result (or this partition's partial).
-  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
-    const int g = idx / D;
+  // Merge the waves of each kv head (waves hs, hs + hpw, ...) and write the
+  // result (or this partition's partial).
+  for (int idx = threadIdx.x; idx < hpw * G * D; idx += NW * 64) {
+    const int hs = idx / (G * D);
+    const int g = (idx / D) % G;
     const int d = idx % D;
-    float M = s_m[0][g];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, s_m[w][g]);
+    float M = s_m[hs][g];
+    for (int w = hs + hpw; w < NW; w += hpw) M = fmaxf(M, s_m[w][g]);
     const float ms = (M == -INFINITY) ? 0.f : M;
     float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int w = hs; w < NW; w += hpw) {
       const float f = fast_exp2(s_m[w][g] - ms);
       L = fmaf(f, s_l[w][g], L);
       O = fmaf(f, s_acc[w][g][d], O);
     }
-    const int h = kvh * G + g;
+    const int h = (kvh0 + hs) * G + g;
     const int64_t sh = static_cast<int64_t>(seq) * a.num_heads + h;
     if (direct) {
       store_elem<QF>(a.out, sh * D + d, L > 0.f ? O / L : 0.f);
