@@ -298,7 +298,8 @@ int pkv_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 typedef struct pkv_allocator pkv_allocator;
 
 /* A pool of num_blocks blocks of block_size tokens; free list = 0..N-1, and
- * blocks leave from its END (the first allocation returns N-1). */
+ * blocks leave from its END (the first allocation returns N-1).  INVALID_ARG
+ * when num_blocks * block_size exceeds INT32_MAX (slots are int32). */
 int pkv_allocator_create(int num_blocks, int block_size, pkv_allocator** out);
 int pkv_allocator_destroy(pkv_allocator* a);
 

@@ -95,6 +95,10 @@ int pkv_allocator_create(int num_blocks, int block_size, pkv_allocator** out) {
   if (num_blocks <= 0 || block_size <= 0)
     return pkv::fail(PKV_ERR_INVALID_ARG, "num_blocks (%d) and block_size (%d) must be positive",
                      num_blocks, block_size);
+  // Slots (block * block_size + offset) are int32 in the slot mapping.
+  if (static_cast<int64_t>(num_blocks) * block_size > INT32_MAX)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "num_blocks * block_size (%lld) exceeds the int32 slot "
+                     "range", static_cast<long long>(num_blocks) * block_size);
   auto* a = new pkv_allocator();
   a->num_blocks = num_blocks;
   a->block_size = block_size;
