@@ -79,9 +79,12 @@ int pkv_abi_version(void);
  * span = max_blocks_per_seq * block_size rounded up to U, a span of up to 2560
  * tokens is not split, a longer one is split into 1024-token partitions, and
  * the partitions are made smaller (in steps of U) until
- * num_seqs * num_kv_heads * partitions >= 512.  With a sliding window W the
- * span is at most W + U - 1 (rounded up to U), and the partitions of a
- * sequence start at its first attended token rounded down to U.
+ * num_seqs * num_kv_heads * partitions >= 512.  With a sliding window W that
+ * is shorter than the table, the span is W + U - 1 rounded up to U, it is not
+ * split by length (every context longer than W attends exactly W tokens),
+ * and it is split into equal partitions only until
+ * num_seqs * num_kv_heads * partitions >= 256.  The partitions of a sequence
+ * start at its first attended token rounded down to U.
  */
 int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
                               int head_dim, int block_size,
@@ -131,8 +134,7 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  *   kv_dtype     F32 (q F32), F16 (q F16), BF16 (q BF16), I8 or FP8 (q F16
  *                or BF16)
  *   head_dim     64 or 128; block_size 8, 16 or 32 ([P1] deployment section:
- *                16 by default; one-byte caches with head_dim 64, block size
- *                8 and num_heads == num_kv_heads are not built: UNSUPPORTED);
+ *                16 by default);
  *                num_heads / num_kv_heads in {1, 2, 4, 8, 16}
  *   partition_size  tokens per partition, a multiple of max(block_size, 16), or 0 for
  *                the library's choice; a value >= the longest possible context

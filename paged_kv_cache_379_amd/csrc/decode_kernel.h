@@ -269,11 +269,14 @@ struct DecodeTile {
   static constexpr int kRow = D * kEB;        // bytes of one (token, kv head) row
   static constexpr int kLPR = kRow / 16;      // lanes per row
   static constexpr int kRPI = 64 / kLPR;      // rows per load instruction
-  static constexpr int kIPB = BS / kRPI;      // load instructions per block
+  // Load instructions per block.  One-byte rows of head_dim 64 give 16 rows
+  // per instruction, more than an 8-token block holds: the row groups past
+  // the block then re-read the block's rows (rg % BS, so every load stays in
+  // the block) and are masked like slots past the context.
+  static constexpr int kIPB = kRPI <= BS ? BS / kRPI : 1;
   static constexpr int kE = 16 / kEB;         // elements per lane per load
-  // Whether one load instruction's rows fit in a block (not so for one-byte
-  // rows of head_dim 64 in 8-token blocks: that combination is not built).
-  static constexpr bool kBuilt = kRPI <= BS && BS % kRPI == 0;
+  static constexpr bool kDupRows = kRPI > BS;
+  static constexpr bool kBuilt = kDupRows ? kRPI % BS == 0 : BS % kRPI == 0;
   static_assert(kRow % 16 == 0 && kLPR >= 1 && kLPR <= 64 && 64 % kLPR == 0, "row shape");
 };
 
@@ -327,8 +330,9 @@ __device__ __forceinline__ void process_blocks(
     }
     const float sc = scale_log2 * ksc[b];
     // tokens lo <= offset < valid of the block are attended (lo > 0 only in
-    // the first block of a sliding window)
-    const bool partial = valid[b] < BS || lo[b] > 0;
+    // the first block of a sliding window); offsets >= BS are the re-read
+    // rows of T::kDupRows
+    const bool partial = T::kDupRows || valid[b] < BS || lo[b] > 0;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -482,7 +486,8 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
 
   const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * T::kRow;
   const int64_t blk_stride = row_stride * BS;
-  const int64_t lane_off = static_cast<int64_t>(kvh) * T::kRow + sub * 16 + rg * row_stride;
+  const int row = T::kDupRows ? rg % BS : rg;
+  const int64_t lane_off = static_cast<int64_t>(kvh) * T::kRow + sub * 16 + row * row_stride;
   const uint8_t* kbase = a.key_cache + lane_off;
   const uint8_t* vbase = a.value_cache + lane_off;
 

@@ -90,12 +90,21 @@ def test_workspace_size_and_partition_policy():
     assert pkv.decode_workspace_size(32, 64, 64, 128, 16, 128, 4096) == 0
     assert pkv.decode_partition_size(2, 4, 4, 64, 16, 7, 32) == 32
     assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7, 32) == 2 * 4 * 4 * 66 * 4
-    # a sliding window sizes partitions by the blocks the window can touch,
-    # ceil((W - 1) / 16) + 1, not by the table
-    assert pkv.decode_partition_size(32, 32, 8, 128, 16, 1024, 0, 4096) == 1024   # 257 blocks
-    assert pkv.decode_workspace_size(32, 32, 8, 128, 16, 1024, 0, 4096) == 32 * 32 * 5 * 130 * 4
-    assert pkv.decode_partition_size(64, 32, 8, 128, 16, 1024, 0, 2048) == 0      # 129 blocks
-    assert pkv.decode_workspace_size(64, 32, 8, 128, 16, 1024, 0, 2048) == 0
+    # a sliding window sizes partitions by the tokens the window can touch,
+    # W + 15 rounded up to 16, not by the table; a window keeps each context
+    # whole while there are at least 256 (sequence, kv head) pairs ...
+    assert pkv.decode_partition_size(32, 32, 8, 128, 16, 1024, 0, 4096) == 0      # 4112 tokens
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 16, 1024, 0, 4096) == 0
+    assert pkv.decode_partition_size(64, 32, 8, 128, 16, 1024, 0, 2048) == 0      # 2064 tokens
+    assert pkv.decode_workspace_size(64, 32, 8, 128, 16, 1024, 0, 8192) == 0
+    # ... and below that splits it into equal partitions until there are
+    # 256 workgroups (128 pairs -> 2 partitions of 2056 -> 2064 tokens)
+    assert pkv.decode_partition_size(16, 32, 8, 128, 16, 1024, 0, 4096) == 2064
+    assert pkv.decode_workspace_size(16, 32, 8, 128, 16, 1024, 0, 4096) == 16 * 32 * 2 * 130 * 4
+    assert pkv.decode_partition_size(1, 8, 8, 128, 16, 1024, 0, 4096) == 144      # 29 parts
+    # a window as long as the table binds nothing: the policy without a window
+    assert pkv.decode_partition_size(256, 32, 8, 128, 16, 256, 0, 4096) == 1024
+    assert pkv.decode_partition_size(256, 32, 8, 128, 16, 256, 0, 5000) == 1024
     assert pkv.decode_workspace_size(32, 32, 8, 128, 16, 1024, 0, -1) == 0        # invalid
     # not a multiple of the block size -> invalid -> 0
     assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7, 40) == 0
@@ -119,8 +128,10 @@ def test_partition_policy_other_block_sizes():
     assert pkv.decode_partition_size(2, 4, 4, 64, 8, 8, 8) == 0  # 8 tokens: not a multiple of 16
     assert pkv.decode_partition_size(2, 4, 4, 64, 32, 8, 16) == 0
     assert pkv.decode_partition_size(2, 4, 4, 64, 32, 8, 64) == 64
-    # a window of 4096 with 32-token blocks: span 4096 + 31 rounded up to 32 = 4128
-    assert pkv.decode_workspace_size(32, 32, 8, 128, 32, 512, 0, 4096) == 32 * 32 * 5 * 130 * 4
+    # a window of 4096 with 32-token blocks: span 4096 + 31 rounded up to 32 =
+    # 4128, whole at 256 pairs, halved (2064 tokens) at 128
+    assert pkv.decode_workspace_size(32, 32, 8, 128, 32, 512, 0, 4096) == 0
+    assert pkv.decode_partition_size(16, 32, 8, 128, 32, 512, 0, 4096) == 2080
     assert pkv.decode_partition_size(2, 4, 4, 64, 12, 8) == 0   # block size not built
 
 

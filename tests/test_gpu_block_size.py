@@ -14,12 +14,6 @@ pytestmark = pytest.mark.gpu
 LENS = [1, 7, 8, 9, 17, 300, 513, 700]
 
 
-def _built(kv_fmt, head_dim, group, bs):
-    """One-byte rows of head_dim 64 fill 16 rows per load instruction, more
-    than an 8-token block: that multi-head combination is not built."""
-    return not (kv_fmt in ("i8", "fp8") and head_dim == 64 and group == 1 and bs == 8)
-
-
 @pytest.mark.parametrize("bs", [8, 32])
 @pytest.mark.parametrize("kv_fmt,q_fmt", [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"),
                                           ("i8", "f16"), ("fp8", "bf16")])
@@ -28,9 +22,9 @@ def _built(kv_fmt, head_dim, group, bs):
 def test_block_size_parity(gpu_lib, bs, kv_fmt, q_fmt, head_dim, group):
     """Every kernel at block sizes 8 and 32: ragged lengths around the block
     and tile boundaries, whole contexts and 32-token partitions, poisoned
-    unread slots and table padding."""
-    if not _built(kv_fmt, head_dim, group, bs):
-        pytest.skip("one-byte head_dim 64 multi-head decode is not built for 8-token blocks")
+    unread slots and table padding.  One-byte multi-head rows of head_dim 64
+    at 8-token blocks fill 16 rows per load instruction, two blocks' worth:
+    the rows past the block are re-read and masked."""
     wl = W.make_workload(2, seed=11 + group + bs, num_seqs=len(LENS), num_heads=2 * group,
                          num_kv_heads=2, head_dim=head_dim, kv_fmt=kv_fmt, q_fmt=q_fmt,
                          ctx=("fixed", LENS), max_blocks=-(-700 // bs) + 3, block_size=bs,
@@ -42,12 +36,22 @@ def test_block_size_parity(gpu_lib, bs, kv_fmt, q_fmt, head_dim, group):
                       label=f"bs={bs} {kv_fmt}/{q_fmt} D={head_dim} G={group} part={part}")
 
 
-def test_unbuilt_combination_is_an_error(gpu_lib):
-    wl = W.make_workload(2, num_seqs=2, num_heads=2, num_kv_heads=2, head_dim=64, kv_fmt="i8",
-                         q_fmt="f16", ctx=("fixed", [5, 9]), max_blocks=4, block_size=8)
-    with pytest.raises(pkv_mod.PkvError) as e:
-        gpu_decode(gpu_lib, wl)
-    assert e.value.code == pkv_mod.ERR_UNSUPPORTED
+@pytest.mark.parametrize("kv_fmt,q_fmt", [("i8", "f16"), ("fp8", "bf16")])
+def test_one_byte_head_dim_64_small_blocks(gpu_lib, kv_fmt, q_fmt):
+    """One-byte multi-head rows of head_dim 64 in 8-token blocks: every length
+    from 1 to 44 (each offset of the last block, up to six blocks), whole and
+    split contexts; with 16-token partitions 8 and 16 kv heads put two and
+    four kv heads in a workgroup."""
+    for hkv in (1, 8, 16):
+        wl = W.make_workload(2, seed=40 + hkv, num_seqs=44, num_heads=hkv, num_kv_heads=hkv,
+                             head_dim=64, kv_fmt=kv_fmt, q_fmt=q_fmt,
+                             ctx=("fixed", list(range(1, 45))), max_blocks=6, block_size=8,
+                             poison_unused=True)
+        ref = oracle_decode(wl)
+        for part in (0, 16):
+            got = out_f64(gpu_decode(gpu_lib, wl, partition_size=part))
+            assert_parity(got, ref, kv_fmt, q_fmt, with_output_rounding=True,
+                          label=f"{kv_fmt} Hkv={hkv} part={part}")
 
 
 @pytest.mark.parametrize("bs", [8, 32])
