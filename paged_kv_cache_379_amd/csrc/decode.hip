@@ -10,12 +10,16 @@
 
 namespace pkv_dev {
 
+// rows: num_seqs * num_heads, kMergeRows per workgroup.
 template <int QF>
-hipError_t launch_reduce(int head_dim, const DecodeArgs& a, unsigned grid, hipStream_t s) {
+hipError_t launch_reduce(int head_dim, const DecodeArgs& a, int64_t rows, hipStream_t s) {
+  if ((rows + kMergeRows - 1) / kMergeRows > INT32_MAX) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>((rows + kMergeRows - 1) / kMergeRows));
+  const dim3 block(kMergeRows * 64);
   if (head_dim == 64)
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<QF, 64>), dim3(grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<QF, 64>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<QF, 128>), dim3(grid), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<QF, 128>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -336,7 +340,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
   if (err != hipSuccess)
     return pkv::fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
   if (parts > 1) {
-    const unsigned rgrid = static_cast<unsigned>(static_cast<int64_t>(num_seqs) * num_heads);
+    const int64_t rgrid = static_cast<int64_t>(num_seqs) * num_heads;
     switch (q_dtype) {
       case PKV_F32: err = pkv_dev::launch_reduce<PKV_F32>(head_dim, a, rgrid, s); break;
       case PKV_F16: err = pkv_dev::launch_reduce<PKV_F16>(head_dim, a, rgrid, s); break;
@@ -496,7 +500,7 @@ int pkv_paged_attention_decode_prefix(void* out, const void* q, const void* key_
       return pkv::fail(PKV_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
   }
   if (!a.merge_prefix) {
-    const unsigned rgrid = static_cast<unsigned>(static_cast<int64_t>(num_seqs) * num_heads);
+    const int64_t rgrid = static_cast<int64_t>(num_seqs) * num_heads;
     switch (q_dtype) {
       case PKV_F16: err = pkv_dev::launch_reduce<PKV_F16>(head_dim, a, rgrid, s); break;
       default: err = pkv_dev::launch_reduce<PKV_BF16>(head_dim, a, rgrid, s); break;

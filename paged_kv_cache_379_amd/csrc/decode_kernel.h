@@ -596,31 +596,70 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   }
 }
 
-// Merge the partitions of each (sequence, head): one workgroup of D threads.
+// Merge the partitions of each (sequence, head): one wave per row, kMergeRows
+// rows per workgroup.  The lanes read the partials' (max, sum) pairs together
+// and two wave reductions give the common exponent base and the sum; then
+// every lane sums its D / 64 dims of the accumulators, issuing the loads of
+// four partials at a time.
+constexpr int kMergeRows = 4;
+
 template <int QF, int D>
-__global__ void __launch_bounds__(D) paged_decode_reduce_kernel(DecodeArgs a) {
-  const int sh = blockIdx.x;  // seq * num_heads + head
-  const int seq = sh / a.num_heads;
+__global__ void __launch_bounds__(kMergeRows * 64) paged_decode_reduce_kernel(DecodeArgs a) {
+  static_assert(D % 64 == 0, "head_dim must be a multiple of the wave");
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t sh = static_cast<int64_t>(blockIdx.x) * kMergeRows + (threadIdx.x >> 6);
+  if (sh >= static_cast<int64_t>(a.num_seqs) * a.num_heads) return;  // seq * num_heads + head
+  const int seq = static_cast<int>(sh / a.num_heads);
   const Span sp = attended_span(a, seq);
   // The partials to merge: the prefix chunks (slots 0 .. nchunks - 1) and the
   // partitions of the rest (slots part_base .. part_base + nparts - 1).
   if (!a.prefix_lens && sp.nparts <= 1) return;  // the decode kernel wrote this output
-  const int d = threadIdx.x;
-  const float* ml = a.ws_ml + static_cast<int64_t>(sh) * a.num_parts * 2;
-  const float* acc = a.ws_acc + static_cast<int64_t>(sh) * a.num_parts * D;
+  const float* ml = a.ws_ml + sh * a.num_parts * 2;
+  const float* acc = a.ws_acc + sh * a.num_parts * D;
   auto slot_of = [&](int i) { return i < sp.nchunks ? i : a.part_base + (i - sp.nchunks); };
   const int n = sp.nchunks + sp.nparts;
+
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, ml[2 * slot_of(i)]);
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, ml[2 * slot_of(i)]);
+  M = across_groups_max<1>(M);
   const float ms = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, O = 0.f;
-  for (int i = 0; i < n; ++i) {
+  float L = 0.f;
+  for (int i = lane; i < n; i += 64) {
     const int p = slot_of(i);
-    const float f = fast_exp2(ml[2 * p] - ms);
-    L = fmaf(f, ml[2 * p + 1], L);
-    O = fmaf(f, acc[static_cast<int64_t>(p) * D + d], O);
+    L = fmaf(fast_exp2(ml[2 * p] - ms), ml[2 * p + 1], L);
   }
-  store_elem<QF>(a.out, static_cast<int64_t>(sh) * D + d, L > 0.f ? O / L : 0.f);
+  L = across_groups_sum<1>(L);
+
+  float O[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) O[e] = 0.f;
+  constexpr int U = 4;
+  int i = 0;
+  for (; i + U <= n; i += U) {
+    float f[U], x[U][E];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = slot_of(i + u);
+      f[u] = ml[2 * p];
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[u][e] = acc[static_cast<int64_t>(p) * D + 64 * e + lane];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float w = fast_exp2(f[u] - ms);
+#pragma unroll
+      for (int e = 0; e < E; ++e) O[e] = fmaf(w, x[u][e], O[e]);
+    }
+  }
+  for (; i < n; ++i) {
+    const int p = slot_of(i);
+    const float w = fast_exp2(ml[2 * p] - ms);
+#pragma unroll
+    for (int e = 0; e < E; ++e) O[e] = fmaf(w, acc[static_cast<int64_t>(p) * D + 64 * e + lane], O[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) store_elem<QF>(a.out, sh * D + 64 * e + lane, L > 0.f ? O[e] / L : 0.f);
 }
 
 }  // namespace pkv_dev
