@@ -42,17 +42,18 @@ def _full(index):
     return _FULL[index]
 
 
-@pytest.mark.parametrize("index", [2, 3, 4, 5, 7, 8])
+@pytest.mark.parametrize("index", [2, 3, 4, 5, 6, 7, 8])
 def test_config_parity_full_size_sampled(gpu_lib, index):
     """Full-size configuration in the benchmark's launch configuration (automatic
-    partitions); the oracle checks a sample of sequences, every head."""
+    partitions; the sliding-window layer with its window, whole windows); the
+    oracle checks a sample of sequences, every head."""
     wl = _full(index)
-    got = out_f64(gpu_decode(gpu_lib, wl))
+    got = out_f64(gpu_decode(gpu_lib, wl, window=wl.window))
     rng = np.random.default_rng(1000 + index)
     seqs = np.sort(rng.choice(wl.num_seqs, size=min(6, wl.num_seqs), replace=False))
     # always include the longest and the shortest sequence
     seqs = np.unique(np.concatenate([seqs, [np.argmax(wl.context_lens), np.argmin(wl.context_lens)]]))
-    ref = oracle_decode(wl, seqs)
+    ref = oracle_decode(wl, seqs, window=wl.window)
     err = assert_parity(got[seqs], ref, wl.kv_fmt, label=f"config {index} full, seqs {seqs}")
     assert np.isfinite(got).all()
     print(f"config {index} full size: sampled seqs {seqs.tolist()} max abs err {err:.3g}")
