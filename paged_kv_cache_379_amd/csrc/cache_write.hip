@@ -8,10 +8,11 @@
 //
 // A new token's K and V rows ([Hkv][D], contiguous in the source and in the
 // cache slot, by the layout of the [P1] kernel sketch) are written to
-// block slot / bs, offset slot % bs.  One workgroup per (token, K or V) moves
-// the row with 16-byte loads and stores; an int8 cache quantises on the way
-// with the (block, kv head) scale ([P2] INT8 KV cache section; scale
-// granularity is this library's reading).
+// block slot / bs, offset slot % bs.  Workgroups per (token, K or V, slice of
+// kWriteThreads 16-byte vectors of the row) move the row with one 16-byte load
+// and store per thread, so a write costs one memory round trip; an int8 cache
+// quantises on the way with the (block, kv head) scale ([P2] INT8 KV cache
+// section; scale granularity is this library's reading).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -78,12 +79,15 @@ __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(CacheWriteAr
   const uint8_t* src = is_v ? a.v : a.k;
   uint8_t* dst = is_v ? a.value_cache : a.key_cache;
   const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * a.head_dim;
+  // this thread's 16-byte vector (float caches) or 16-element chunk (one-byte
+  // caches) of the row
+  const int64_t c = static_cast<int64_t>(blockIdx.z) * kWriteThreads + threadIdx.x;
   if constexpr (!pkv_dev::scaled_format(KF)) {
     static_assert(SF == KF, "float caches take rows of their own format");
     const int64_t vecs = row_elems * Format<KF>::kBytes / 16;
     const uint4* s4 = reinterpret_cast<const uint4*>(src) + t * vecs;
     uint4* d4 = reinterpret_cast<uint4*>(dst) + static_cast<int64_t>(slot) * vecs;
-    for (int64_t c = threadIdx.x; c < vecs; c += kWriteThreads) d4[c] = s4[c];
+    if (c < vecs) d4[c] = s4[c];
   } else {
     const float* scales = is_v ? a.v_scales : a.k_scales;
     const int blk = slot / a.block_size;
@@ -91,7 +95,7 @@ __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(CacheWriteAr
     const int64_t chunks = row_elems / 16;
     const uint4* s4 = reinterpret_cast<const uint4*>(src) + t * chunks * kSrcVecs;
     uint4* d4 = reinterpret_cast<uint4*>(dst) + static_cast<int64_t>(slot) * chunks;
-    for (int64_t c = threadIdx.x; c < chunks; c += kWriteThreads) {
+    if (c < chunks) {
       const int kvh = static_cast<int>(c * 16 / a.head_dim);
       const float sc = scales[static_cast<int64_t>(blk) * a.num_kv_heads + kvh];
       float x[16];
@@ -105,9 +109,22 @@ __global__ void __launch_bounds__(kWriteThreads) cache_write_kernel(CacheWriteAr
   }
 }
 
+// Row slices per (token, K or V): one thread per 16-byte vector of a float
+// row, or per 16 elements of a one-byte row.
+template <int SF, int KF>
+int64_t write_slices(const CacheWriteArgs& a) {
+  const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * a.head_dim;
+  const int64_t per_row = pkv_dev::scaled_format(KF) ? row_elems / 16
+                                                     : row_elems * Format<KF>::kBytes / 16;
+  return (per_row + kWriteThreads - 1) / kWriteThreads;
+}
+
 template <int SF, int KF>
 hipError_t launch_write(const CacheWriteArgs& a, int num_tokens, hipStream_t s) {
-  hipLaunchKernelGGL((cache_write_kernel<SF, KF>), dim3(num_tokens, 2), dim3(kWriteThreads), 0, s, a);
+  const int64_t slices = write_slices<SF, KF>(a);
+  if (slices > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((cache_write_kernel<SF, KF>), dim3(num_tokens, 2, static_cast<unsigned>(slices)),
+                     dim3(kWriteThreads), 0, s, a);
   return hipGetLastError();
 }
 
