@@ -260,20 +260,21 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
   }
 
   // V^T operands, read first so that their latency hides behind the scores
-  // and the softmax: lane (t, g) reads V elements (row 4g + j, dim 16c + t),
-  // j < 4, straight into the low and high halves of two registers.
+  // and the softmax: lane (t, g) needs V elements (row 4g + j, dim 16c + t),
+  // j < 4, in the four 16-bit halves of two registers.  gfx950's transposing
+  // LDS read delivers them in one instruction per 16 dims: within each group
+  // of 16 lanes, lane 4a + b receives element b of the 8-byte pieces that
+  // lanes a, a + 4, a + 8 and a + 12 address (checked on the device), so lane
+  // (t, g) addresses row 4g + t / 4, dims 16c + 4 (t % 4) .. + 3.
   u32x2_t vt[T::kTiles];
   {
-    const uint8_t* vcol = tile + T::kTile + 4 * g * T::kPitch + 2 * t;
+    typedef short i16x4_lds_t __attribute__((ext_vector_type(4)));
+    const uint8_t* vp = tile + T::kTile + (4 * g + t / 4) * T::kPitch + 8 * (t % 4);
 #pragma unroll
     for (int c = 0; c < T::kTiles; ++c) {
-      const uint8_t* p = vcol + 32 * c;
-      half2_t lo, hi;
-      lo.x = *reinterpret_cast<const _Float16*>(p);
-      lo.y = *reinterpret_cast<const _Float16*>(p + T::kPitch);
-      hi.x = *reinterpret_cast<const _Float16*>(p + 2 * T::kPitch);
-      hi.y = *reinterpret_cast<const _Float16*>(p + 3 * T::kPitch);
-      vt[c] = u32x2_t{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      const i16x4_lds_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_lds_t*)(vp + 32 * c));
+      vt[c] = __builtin_bit_cast(u32x2_t, r);
     }
   }
 
