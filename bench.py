@@ -18,7 +18,12 @@ synchronisations).  ``roofline`` reports the decode call (the dominant
 kernel) against HBM bandwidth: algorithmic bytes per call (K and V of every
 context token read once, each shared block counted once, plus Q, the output,
 the block-table entries, the lengths and int8 scales) over its average
-duration from HIP events on the launch stream.  ``cpu_baseline`` times the CPU
+duration from HIP events on the launch stream.  The timed steps rotate
+through identical copies of the K/V caches (``cache_copies``, enough that at
+least 768 MiB of other cache data passes between two uses of one copy), so a
+step reads its K/V from HBM, not from the MALL the previous step filled; the
+event-timed sweeps fill a 512 MiB buffer before each timed call for the same
+reason.  ``cpu_baseline`` times the CPU
 oracle (test infrastructure, fp64 NumPy) on a bounded sample of the same
 workload on this host.
 """
@@ -43,6 +48,20 @@ TOL = {"f32": 1e-4, "f16": 2e-3, "bf16": 2e-3, "i8": 2e-2, "fp8": 2e-3}
 KERNEL_SOURCES = ["decode_kernel.h", "decode_gqa_kernel.h", "decode_prefix_kernel.h",
                   "decode_dispatch.h", "decode.hip", "decode_f32.hip", "decode_f16.hip",
                   "decode_bf16.hip", "decode_i8.hip", "decode_fp8.hip"]
+
+
+# Caches between timed calls: each XCD's L2 (4 MiB) and the 256 MiB MALL in
+# front of HBM.  A call reads its K/V cold when at least COLD_BYTES of other
+# data went through them since its last use.
+COLD_BYTES = 768 << 20
+FLUSH_BYTES = 512 << 20
+
+
+def cache_copies(kv_bytes):
+    """Copies of the K/V caches that the timed steps rotate through, so that
+    every step reads its K/V from HBM rather than from the MALL that the
+    previous step filled (at most 16)."""
+    return int(min(16, max(1, math.ceil(COLD_BYTES / max(kv_bytes, 1)))))
 
 
 def kernel_hash():
@@ -278,6 +297,7 @@ def block_size_sweep(args, torch, pkv, W, log):
 
     rows = {}
     name = None
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     for bs in (8, 16, 32):
         wl = W.make_workload(args.config, seed=args.seed, block_size=bs,
                              max_blocks=-(-mb16 * 16 // bs))
@@ -303,6 +323,7 @@ def block_size_sweep(args, torch, pkv, W, log):
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         for e0, e1 in ev:
+            flush.fill_(1)   # the caches start cold, outside the timed span
             e0.record()
             decode()
             e1.record()
@@ -367,6 +388,8 @@ def shared_prefix_sweep(args, torch, pkv, W, log):
             return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(arr).to(dev)
 
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
     def timed(fn):
         for _ in range(args.warmup):
             fn()
@@ -374,6 +397,7 @@ def shared_prefix_sweep(args, torch, pkv, W, log):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
         for e0, e1 in ev:
+            flush.fill_(1)   # the caches start cold, outside the timed span
             e0.record()
             fn()
             e1.record()
@@ -521,34 +545,46 @@ def main():
         need = pkv.decode_prefix_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, groups)
         prefix_lens = torch.full((B,), groups[0][2], dtype=torch.int32, device=dev)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ab = algorithmic_bytes(wl)
+    # Identical copies of the caches, used in turn: a step then finds none of
+    # its K/V in the MALL or L2 that the steps before it filled, as in serving,
+    # where the other layers' caches pass through between two decodes of one
+    # layer.  Every copy receives every cache write, so all stay identical.
+    copies = cache_copies(ab["kv"])
+    sets = [(kc, vc, ks, vs)]
+    for _ in range(copies - 1):
+        sets.append(tuple(None if x is None else x.clone() for x in (kc, vc, ks, vs)))
     torch.cuda.synchronize()
 
-    def write():
-        pkv.reshape_and_cache(k_new, v_new, kc, vc, slots, ks, vs)
+    def write(i=0):
+        kci, vci, ksi, vsi = sets[i % copies]
+        pkv.reshape_and_cache(k_new, v_new, kci, vci, slots, ksi, vsi)
 
-    def decode():
+    def decode(i=0):
+        kci, vci, ksi, vsi = sets[i % copies]
         if groups:
-            pkv.paged_attention_decode_prefix(out, q, kc, vc, tables, lens, wl.block_size, wl.scale,
-                                              groups, ks, vs, workspace=ws, prefix_lens=prefix_lens)
+            pkv.paged_attention_decode_prefix(out, q, kci, vci, tables, lens, wl.block_size,
+                                              wl.scale, groups, ksi, vsi, workspace=ws,
+                                              prefix_lens=prefix_lens)
         else:
-            pkv.paged_attention_decode(out, q, kc, vc, tables, lens, wl.block_size, wl.scale, ks,
-                                       vs, partition_size=args.partition, workspace=ws,
+            pkv.paged_attention_decode(out, q, kci, vci, tables, lens, wl.block_size, wl.scale, ksi,
+                                       vsi, partition_size=args.partition, workspace=ws,
                                        window=wl.window)
 
-    for _ in range(args.warmup):
-        write()
-        decode()
+    for i in range(max(args.warmup, copies)):
+        write(i)
+        decode(i)
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+    log(f"warmup done; timing {args.steps} steps over {copies} cache copies")
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record()
-        write()
+        write(i)
         ev[i][1].record()
-        decode()
+        decode(i)
         ev[i][2].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -572,7 +608,6 @@ def main():
     copy_gbps = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
     del src, dst
 
-    ab = algorithmic_bytes(wl)
     ctx_per_step = ab["logical_tokens"]
     value = ctx_per_step * args.steps / elapsed
     achieved = ab["total"] / (decode_us * 1e-6) / 1e9
@@ -608,6 +643,7 @@ def main():
         },
         "decode_tokens_per_s": ctx_per_step / (decode_us * 1e-6),
         "cache_write_us": write_us,
+        "cache_copies": copies,
         "copy_probe_gbps": copy_gbps,
         "decode_frac_of_copy_probe": achieved / copy_gbps,
         "kernel_hash": kernel_hash(),
