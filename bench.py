@@ -60,8 +60,12 @@ FLUSH_BYTES = 512 << 20
 def cache_copies(kv_bytes):
     """Copies of the K/V caches that the timed steps rotate through, so that
     every step reads its K/V from HBM rather than from the MALL that the
-    previous step filled (at most 16)."""
-    return int(min(16, max(1, math.ceil(COLD_BYTES / max(kv_bytes, 1)))))
+    previous steps filled: the other copies' K/V, at least COLD_BYTES, pass
+    between two uses of one copy (at most 16 copies).  K/V of COLD_BYTES or
+    more evicts itself within one call: one copy."""
+    if kv_bytes >= COLD_BYTES:
+        return 1
+    return int(min(16, 1 + math.ceil(COLD_BYTES / max(kv_bytes, 1))))
 
 
 def kernel_hash():
