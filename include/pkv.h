@@ -290,6 +290,19 @@ int pkv_swap_blocks(void* key_cache, void* value_cache, float* k_scales, float* 
  */
 int pkv_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/*
+ * Read-only streaming probe over `bytes` bytes of device memory at `src` (a
+ * multiple of 16, 16-byte aligned) with the decode's loads (16-byte,
+ * non-temporal): the reference point for the read bandwidth a decode can
+ * reach.  Each thread folds the words it read with XOR and writes the fold to
+ * the device word `sink` only when it equals `sentinel`, so that no load can
+ * be optimised away; `sink` must be a writable device word (its content
+ * after the call is unspecified unless some fold equals the sentinel).
+ * Errors: INVALID_ARG (NULL, misaligned, size), HIP.
+ */
+int pkv_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t sentinel,
+                    void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block allocator ([P3] section 二: BlockManager / BlockTable; [P1]     */
 /* "PagedAttention分页内存管理原理" and "vLLM调度器与PagedAttention协同工作"). */

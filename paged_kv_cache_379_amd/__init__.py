@@ -17,7 +17,8 @@ __all__ = [
     "load", "LIB_PATH", "PkvError", "OutOfBlocks", "DoubleFree",
     "paged_attention_decode", "decode_workspace_size", "decode_partition_size",
     "paged_attention_decode_prefix", "decode_prefix_workspace_size", "find_shared_prefixes",
-    "reshape_and_cache", "copy_blocks", "swap_blocks", "stream_copy", "validate_tables",
+    "reshape_and_cache", "copy_blocks", "swap_blocks", "stream_copy", "stream_read",
+    "validate_tables",
     "BlockAllocator", "F32", "F16", "BF16", "I8", "FP8", "SWAP_OUT", "SWAP_IN",
 ]
 
@@ -61,6 +62,7 @@ _SIGS = {
     "pkv_copy_blocks": (_c_int, [_vp] * 4 + [_i32p, _c_int, _c_size, _c_int, _c_int, _vp]),
     "pkv_swap_blocks": (_c_int, [_vp] * 8 + [_i32p, _c_int, _c_size] + [_c_int] * 4 + [_vp]),
     "pkv_stream_copy": (_c_int, [_vp, _vp, _c_size, _vp]),
+    "pkv_stream_read": (_c_int, [_vp, _c_size, _vp, ctypes.c_uint32, _vp]),
     "pkv_allocator_create": (_c_int, [_c_int, _c_int, ctypes.POINTER(_vp)]),
     "pkv_allocator_destroy": (_c_int, [_vp]),
     "pkv_allocator_set_free_order": (_c_int, [_vp, _i32p, _c_int]),
@@ -381,6 +383,16 @@ def stream_copy(dst, src, nbytes=None, stream=None):
     lib = load()
     nbytes = nbytes if nbytes is not None else src.numel() * src.element_size()
     _check(lib.pkv_stream_copy(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), nbytes, _stream(stream)))
+
+
+def stream_read(src, sink, nbytes=None, sentinel=0x9E3779B9, stream=None):
+    """The library's read-only streaming probe (read bandwidth reference);
+    sink: a device int32 tensor, written only if a thread's XOR fold of the
+    words it read equals the sentinel."""
+    lib = load()
+    nbytes = nbytes if nbytes is not None else src.numel() * src.element_size()
+    _check(lib.pkv_stream_read(_dev_ptr(src, "src"), nbytes, _dev_ptr(sink, "sink"),
+                               int(sentinel) & 0xFFFFFFFF, _stream(stream)))
 
 
 def validate_tables(tables, lens, block_size, num_blocks, window=0):

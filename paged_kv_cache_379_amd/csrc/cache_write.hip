@@ -273,6 +273,34 @@ __global__ void __launch_bounds__(kStreamThreads) stream_copy_kernel(uint4* __re
   for (; i < nvec; i += stride) dst[i] = src[i];
 }
 
+// Read-only streaming probe with the decode's loads (16-byte, non-temporal),
+// eight in flight per thread.  Each thread folds what it read with XOR and
+// stores the fold to the sink only if it equals the sentinel, a run-time
+// value, so no load can be dropped.
+constexpr int kReadUnroll = 8;
+
+__global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const uint4* __restrict__ src,
+                                                                     int64_t nvec, uint32_t* sink,
+                                                                     uint32_t sentinel) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kStreamThreads;
+  int64_t i = static_cast<int64_t>(blockIdx.x) * kStreamThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (kReadUnroll - 1) * stride < nvec; i += kReadUnroll * stride) {
+    u32x4 r[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u)
+      r[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i + u * stride));
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
+  }
+  for (; i < nvec; i += stride) {
+    const uint4 r = src[i];
+    acc ^= r.x ^ r.y ^ r.z ^ r.w;
+  }
+  if (acc == sentinel) *sink = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,6 +460,24 @@ int pkv_stream_copy(void* dst, const void* src, size_t bytes, void* stream) {
                      static_cast<const uint4*>(src), nvec);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return pkv::fail(PKV_ERR_HIP, "copy launch: %s", hipGetErrorString(err));
+  return PKV_OK;
+  PKV_API_END
+}
+
+int pkv_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t sentinel,
+                    void* stream) {
+  PKV_API_BEGIN
+  if (bytes == 0) return PKV_OK;
+  if (!src || !sink || bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "NULL or misaligned pointer, or size not a multiple of 16");
+  const int64_t nvec = static_cast<int64_t>(bytes / 16);
+  int64_t blocks = (nvec + kStreamThreads * kReadUnroll - 1) / (kStreamThreads * kReadUnroll);
+  if (blocks > 256 * 32) blocks = 256 * 32;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
+                     0, static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), nvec, sink,
+                     sentinel);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return pkv::fail(PKV_ERR_HIP, "read launch: %s", hipGetErrorString(err));
   return PKV_OK;
   PKV_API_END
 }

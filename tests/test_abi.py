@@ -206,6 +206,10 @@ def test_cache_write_and_copy_reject_bad_arguments():
     ok = np.array([[1, 2]], np.int32)
     assert c(1, 1, None, None, ok.ctypes.data_as(i32p), 1, 4000 + 8, 8, 2, None) == pkv.ERR_INVALID_ARG
     assert lib.pkv_stream_copy(1, 1, 24, None) == pkv.ERR_INVALID_ARG
+    assert lib.pkv_stream_read(16, 24, 16, 0, None) == pkv.ERR_INVALID_ARG    # size
+    assert lib.pkv_stream_read(8, 32, 16, 0, None) == pkv.ERR_INVALID_ARG     # misaligned
+    assert lib.pkv_stream_read(16, 32, None, 0, None) == pkv.ERR_INVALID_ARG  # no sink
+    assert lib.pkv_stream_read(None, 0, None, 0, None) == pkv.OK              # nothing to read
 
 
 def test_swap_rejects_bad_arguments():

@@ -150,3 +150,23 @@ def test_stream_copy(gpu_lib):
     gpu_lib.stream_copy(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def test_stream_read(gpu_lib):
+    """The read probe folds what it reads: with every 16-byte vector holding
+    the words (1, 0, 0, 0), a thread's fold is the parity of the vectors it
+    read, and only a sentinel that some fold equals reaches the sink."""
+    nvec = 3 * 1024 * 1024 // 16 + 3                      # a ragged tail past the unrolled loop
+    words = torch.zeros((nvec, 4), dtype=torch.int32, device="cuda:0")
+    words[:, 0] = 1
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda:0")
+    gpu_lib.stream_read(words, sink, sentinel=2)          # no fold is 2
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    gpu_lib.stream_read(words, sink, sentinel=1)          # threads that read an odd count
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 1
+    zeros = torch.zeros(nvec * 16, dtype=torch.uint8, device="cuda:0")
+    gpu_lib.stream_read(zeros, sink, sentinel=0)          # every fold is 0
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
