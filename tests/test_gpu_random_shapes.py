@@ -3,7 +3,8 @@ format (and query format), head_dim, query heads per kv head, kv heads, block
 size, batch, context lengths (block edges and zero included), an optional
 sliding window and an optional partition size, from its own seed.  The
 shared-prefix cases draw batches of forked prompts and unrelated sequences
-in the block allocator.  The cases reach combinations no hand-written test
+in the block allocator; the cache-write cases draw formats, shapes and slot
+maps with skipped and out-of-pool slots, checked bit for bit.  The cases reach combinations no hand-written test
 names; every one must match the oracle to the format's tolerance.
 """
 import numpy as np
@@ -84,3 +85,42 @@ def test_random_prefix_parity(gpu_lib, k):
     c = _prefix_case(k)
     _run(gpu_lib, np.random.default_rng(c["seed"]), c["kv_fmt"], c["q_fmt"], c["group"],
          c["kv_heads"], c["head_dim"], c["bs"], c["layout"], extra=c["extra"])
+
+
+WRITE_FORMATS = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("i8", "f16"), ("i8", "bf16"),
+                 ("i8", "f32"), ("fp8", "f16"), ("fp8", "bf16"), ("fp8", "f32")]
+
+
+@pytest.mark.parametrize("k", range(40))
+def test_random_cache_write_bit_exact(gpu_lib, k):
+    """reshape_and_cache on a random shape: distinct random slots over the
+    whole pool, some -1 and some past the pool (both skipped)."""
+    import oracle.paged_attention as pa
+    from gpu_util import to_dev, to_host, upload
+    rng = np.random.default_rng(11000 + k)
+    kv_fmt, src_fmt = WRITE_FORMATS[rng.integers(len(WRITE_FORMATS))]
+    bs = int(rng.choice([8, 16, 32]))
+    hkv = int(rng.integers(1, 9))
+    head_dim = int(rng.choice([64, 128]))
+    tokens = int(rng.integers(1, 300))
+    wl = W.make_workload(2, seed=500 + k, num_seqs=tokens, num_heads=hkv, num_kv_heads=hkv,
+                         head_dim=head_dim, kv_fmt=kv_fmt,
+                         q_fmt=src_fmt if kv_fmt in ("i8", "fp8") else kv_fmt,
+                         ctx=("uniform", 1, 64), max_blocks=-(-64 // bs), block_size=bs)
+    n_slots = wl.num_blocks * bs
+    slots = rng.choice(n_slots, size=tokens, replace=False).astype(np.int32)
+    skip = rng.random(tokens) < 0.1
+    slots[skip] = -1
+    past = rng.random(tokens) < 0.05
+    slots[past] = n_slots + rng.integers(0, 1000, int(past.sum()))
+    dev = upload(wl)
+    gpu_lib.reshape_and_cache(dev["k_new"], dev["v_new"], dev["key_cache"], dev["value_cache"],
+                              to_dev(slots, "i32"), dev["k_scales"], dev["v_scales"])
+    import torch
+    torch.cuda.synchronize()
+    kref, vref = pa.reshape_and_cache(wl.k_new, wl.v_new, wl.new_fmt, wl.key_cache,
+                                      wl.value_cache, wl.kv_fmt,
+                                      np.where(slots >= n_slots, -1, slots), bs, wl.k_scales,
+                                      wl.v_scales)
+    np.testing.assert_array_equal(to_host(dev["key_cache"], kv_fmt), kref)
+    np.testing.assert_array_equal(to_host(dev["value_cache"], kv_fmt), vref)
