@@ -20,6 +20,17 @@ constexpr int kMaxGroup = 16;  // query heads per kv head, padded to one 16-wide
 // cores.
 template <int KF, int QF, int D, int G, int BS>
 hipError_t launch_vector(const DecodeArgs& a, unsigned grid, hipStream_t s, bool& ok) {
+  // One-byte rows of head_dim 64 are half a 128-byte line: with an even
+  // number of kv heads per workgroup, each load row covers two neighbouring
+  // heads (HR = 2).
+  if constexpr (G == 1 && Format<KF>::kBytes == 1 && D == 64) {
+    if (a.heads_per_item % 2 == 0) {
+      ok = true;
+      hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, G, kDecodeWaves, BS, 2>), dim3(grid),
+                         dim3(kDecodeWaves * 64), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr (DecodeTile<KF, QF, D, G, kDecodeWaves, BS>::kBuilt) {
     ok = true;
     hipLaunchKernelGGL((paged_decode_kernel<KF, QF, D, G, kDecodeWaves, BS>), dim3(grid),

@@ -263,11 +263,14 @@ __device__ __forceinline__ float across_groups_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <int KF, int QF, int D, int G, int NW, int BS>
+// HR: neighbouring kv heads whose rows one load row covers (2 for one-byte
+// rows of head_dim 64, so that a load row is a whole 128-byte line).
+template <int KF, int QF, int D, int G, int NW, int BS, int HR = 1>
 struct DecodeTile {
   static constexpr int kEB = Format<KF>::kBytes;
-  static constexpr int kRow = D * kEB;        // bytes of one (token, kv head) row
+  static constexpr int kRow = HR * D * kEB;   // bytes of one load row (token, HR kv heads)
   static constexpr int kLPR = kRow / 16;      // lanes per row
+  static constexpr int kLPH = kLPR / HR;      // lanes per head within a row
   static constexpr int kRPI = 64 / kLPR;      // rows per load instruction
   // Load instructions per block.  One-byte rows of head_dim 64 give 16 rows
   // per instruction, more than an 8-token block holds: the row groups past
@@ -289,15 +292,15 @@ struct SoftmaxState {
 };
 
 // Score, mask and accumulate NBLK blocks whose loads are issued together.
-template <int KF, int QF, int D, int G, int NW, int BS, int NBLK>
+template <int KF, int QF, int D, int G, int NW, int BS, int HR, int NBLK>
 __device__ __forceinline__ void process_blocks(
-    SoftmaxState<G, DecodeTile<KF, QF, D, G, NW, BS>::kE>& st,
-    const float (&qf)[G][DecodeTile<KF, QF, D, G, NW, BS>::kE], const uint8_t* kbase,
+    SoftmaxState<G, DecodeTile<KF, QF, D, G, NW, BS, HR>::kE>& st,
+    const float (&qf)[G][DecodeTile<KF, QF, D, G, NW, BS, HR>::kE], const uint8_t* kbase,
     const uint8_t* vbase, int64_t blk_stride, int64_t row_stride, const int (&phys)[NBLK],
     const int (&lo)[NBLK], const int (&valid)[NBLK], const float (&ksc)[NBLK],
     const float (&vsc)[NBLK], int rg, float scale_log2) {
-  using T = DecodeTile<KF, QF, D, G, NW, BS>;
-  constexpr int E = T::kE, IPB = T::kIPB, RPI = T::kRPI, LPR = T::kLPR;
+  using T = DecodeTile<KF, QF, D, G, NW, BS, HR>;
+  constexpr int E = T::kE, IPB = T::kIPB, RPI = T::kRPI, LPH = T::kLPH;
   uint4 kr[NBLK][IPB], vr[NBLK][IPB];
 #pragma unroll
   for (int b = 0; b < NBLK; ++b) {
@@ -337,7 +340,7 @@ __device__ __forceinline__ void process_blocks(
     for (int g = 0; g < G; ++g) {
 #pragma unroll
       for (int i = 0; i < IPB; ++i) {
-        float v = group_sum<LPR>(s[g][i]) * sc;
+        float v = group_sum<LPH>(s[g][i]) * sc;
         const int off = i * RPI + rg;
         if (partial && (off >= valid[b] || off < lo[b])) v = -INFINITY;
         s[g][i] = v;
@@ -403,17 +406,17 @@ __device__ __forceinline__ void store_merged_with_prefix(const DecodeArgs& a, in
   store_elem<QF>(a.out, sh * D + d, L > 0.f ? O / L : 0.f);
 }
 
-template <int KF, int QF, int D, int G, int NW, int BS>
+template <int KF, int QF, int D, int G, int NW, int BS, int HR = 1>
 __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
-  using T = DecodeTile<KF, QF, D, G, NW, BS>;
-  constexpr int E = T::kE, LPR = T::kLPR;
+  using T = DecodeTile<KF, QF, D, G, NW, BS, HR>;
+  constexpr int E = T::kE, LPR = T::kLPR, LPH = T::kLPH;
   // Blocks whose loads are issued together: 32 tokens' worth.
   constexpr int UNROLL = BS >= 32 ? 1 : 32 / BS;
   const int part_blocks = a.part_tokens / BS;
 
-  __shared__ float s_acc[NW][G][D];
-  __shared__ float s_m[NW][G];
-  __shared__ float s_l[NW][G];
+  __shared__ float s_acc[NW][G][HR * D];
+  __shared__ float s_m[NW][HR][G];
+  __shared__ float s_l[NW][HR][G];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -431,11 +434,14 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   // the partition from block w / hpw.  The heads' rows of a block are
   // adjacent in the cache, so one CU then reads hpw x head_dim x element
   // bytes of each token row at about the same time instead of one head's
-  // 128 or 256 bytes.
+  // 128 or 256 bytes.  With HR = 2 a wave's load rows cover two
+  // neighbouring heads (the lanes of a row split between them), so the hpw
+  // heads form hpw / 2 such pairs: wave w takes pair w % (hpw / 2).
   const int hpw = a.heads_per_item;
-  const int wph = NW / hpw;
-  const int hsub = wave % hpw;
-  const int wslot = wave / hpw;
+  const int vpw = hpw / HR;           // head groups (single heads or pairs) per workgroup
+  const int wph = NW / vpw;
+  const int hsub = wave % vpw;
+  const int wslot = wave / vpw;
   const int item = blockIdx.x;
   const int gps = a.num_kv_heads / hpw;
   const int nsk = a.num_seqs * gps;
@@ -443,7 +449,9 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   const int sk = item - part * nsk;
   const int seq = sk / gps;
   const int kvh0 = (sk - seq * gps) * hpw;
-  const int kvh = kvh0 + hsub;
+  const int kvw = kvh0 + hsub * HR;   // the wave's first kv head
+  const int lhead = sub / LPH;        // this lane's head within the load row
+  const int kvh = kvw + lhead;        // this lane's kv head
 
   const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
   // Issued together, before the context length is known, so that the
@@ -465,7 +473,7 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int h = kvh * G + g;
-    load_q<QF, E>(a.q, (static_cast<int64_t>(seq) * a.num_heads + h) * D + sub * E, qf[g]);
+    load_q<QF, E>(a.q, (static_cast<int64_t>(seq) * a.num_heads + h) * D + (sub % LPH) * E, qf[g]);
   }
 
   const Span sp = attended_span(a, seq);
@@ -484,10 +492,11 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
     for (int e = 0; e < E; ++e) st.acc[g][e] = 0.f;
   }
 
-  const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * T::kRow;
+  constexpr int kHeadBytes = D * T::kEB;
+  const int64_t row_stride = static_cast<int64_t>(a.num_kv_heads) * kHeadBytes;
   const int64_t blk_stride = row_stride * BS;
   const int row = T::kDupRows ? rg % BS : rg;
-  const int64_t lane_off = static_cast<int64_t>(kvh) * T::kRow + sub * 16 + row * row_stride;
+  const int64_t lane_off = static_cast<int64_t>(kvw) * kHeadBytes + sub * 16 + row * row_stride;
   const uint8_t* kbase = a.key_cache + lane_off;
   const uint8_t* vbase = a.value_cache + lane_off;
 
@@ -497,17 +506,32 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   for (int k0 = 0; k0 < nk; k0 += 64) {
     const int kk = k0 + lane;
     int tb = -1;
-    float tks = 1.f, tvs = 1.f;
+    // scales of table entry kk for the wave's HR heads (broadcast below,
+    // then each lane takes its own head's)
+    float tks[HR], tvs[HR];
+#pragma unroll
+    for (int r = 0; r < HR; ++r) tks[r] = tvs[r] = 1.f;
     if (kk < nk) {
       tb = (k0 == 0 && early_table) ? tb_first : trow[pb0 + wslot + wph * kk];
       if (static_cast<unsigned>(tb) >= static_cast<unsigned>(a.num_blocks)) tb = -1;
       if constexpr (scaled_format(KF)) {
         if (tb >= 0) {
-          tks = a.k_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];
-          tvs = a.v_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvh];
+#pragma unroll
+          for (int r = 0; r < HR; ++r) {
+            tks[r] = a.k_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvw + r];
+            tvs[r] = a.v_scales[static_cast<int64_t>(tb) * a.num_kv_heads + kvw + r];
+          }
         }
       }
     }
+    auto bcast = [&](const float (&v)[HR], int from) {
+      float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[0]), from));
+      if constexpr (HR == 2) {
+        const float y = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[1]), from));
+        x = lhead ? y : x;
+      }
+      return x;
+    };
     const int kend = min(64, nk - k0);
     int k = 0;
     for (; k + UNROLL <= kend; k += UNROLL) {
@@ -520,11 +544,11 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
         phys[u] = p < 0 ? 0 : p;
         lo[u] = max(0, sp.first - j * BS);
         valid[u] = p < 0 ? 0 : min(BS, ctx - j * BS);
-        ks[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k + u));
-        vs[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k + u));
+        ks[u] = bcast(tks, k + u);
+        vs[u] = bcast(tvs, k + u);
       }
-      process_blocks<KF, QF, D, G, NW, BS, UNROLL>(st, qf, kbase, vbase, blk_stride, row_stride, phys,
-                                               lo, valid, ks, vs, rg, a.scale_log2);
+      process_blocks<KF, QF, D, G, NW, BS, HR, UNROLL>(st, qf, kbase, vbase, blk_stride, row_stride,
+                                                   phys, lo, valid, ks, vs, rg, a.scale_log2);
     }
     for (; k < kend; ++k) {
       const int p = __builtin_amdgcn_readlane(tb, k);
@@ -532,10 +556,10 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
       int phys[1] = {p < 0 ? 0 : p};
       int lo[1] = {max(0, sp.first - j * BS)};
       int valid[1] = {p < 0 ? 0 : min(BS, ctx - j * BS)};
-      float ks[1] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k))};
-      float vs[1] = {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k))};
-      process_blocks<KF, QF, D, G, NW, BS, 1>(st, qf, kbase, vbase, blk_stride, row_stride, phys, lo,
-                                          valid, ks, vs, rg, a.scale_log2);
+      float ks[1] = {bcast(tks, k)};
+      float vs[1] = {bcast(tvs, k)};
+      process_blocks<KF, QF, D, G, NW, BS, HR, 1>(st, qf, kbase, vbase, blk_stride, row_stride, phys,
+                                              lo, valid, ks, vs, rg, a.scale_log2);
     }
   }
 
@@ -555,29 +579,31 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) s_acc[wave][g][sub * E + e] = st.acc[g][e];
   }
-  if (lane == 0) {
+  if (rg == 0 && sub % LPH == 0) {   // the first lane of each head in the row
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      s_m[wave][g] = st.m[g];
-      s_l[wave][g] = st.l[g];
+      s_m[wave][lhead][g] = st.m[g];
+      s_l[wave][lhead][g] = st.l[g];
     }
   }
   __syncthreads();
 
-  // Merge the waves of each kv head (waves hs, hs + hpw, ...) and write the
-  // result (or this partition's partial).
+  // Merge the waves of each kv head (head slot hs is half hs % HR of the
+  // waves hs / HR, hs / HR + vpw, ...) and write the result (or this
+  // partition's partial).
   for (int idx = threadIdx.x; idx < hpw * G * D; idx += NW * 64) {
     const int hs = idx / (G * D);
     const int g = (idx / D) % G;
     const int d = idx % D;
-    float M = s_m[hs][g];
-    for (int w = hs + hpw; w < NW; w += hpw) M = fmaxf(M, s_m[w][g]);
+    const int hw = hs / HR, half = hs % HR;
+    float M = s_m[hw][half][g];
+    for (int w = hw + vpw; w < NW; w += vpw) M = fmaxf(M, s_m[w][half][g]);
     const float ms = (M == -INFINITY) ? 0.f : M;
     float L = 0.f, O = 0.f;
-    for (int w = hs; w < NW; w += hpw) {
-      const float f = fast_exp2(s_m[w][g] - ms);
-      L = fmaf(f, s_l[w][g], L);
-      O = fmaf(f, s_acc[w][g][d], O);
+    for (int w = hw; w < NW; w += vpw) {
+      const float f = fast_exp2(s_m[w][half][g] - ms);
+      L = fmaf(f, s_l[w][half][g], L);
+      O = fmaf(f, s_acc[w][g][half * D + d], O);
     }
     const int h = (kvh0 + hs) * G + g;
     const int64_t sh = static_cast<int64_t>(seq) * a.num_heads + h;

@@ -36,22 +36,39 @@ def test_block_size_parity(gpu_lib, bs, kv_fmt, q_fmt, head_dim, group):
                       label=f"bs={bs} {kv_fmt}/{q_fmt} D={head_dim} G={group} part={part}")
 
 
+@pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("kv_fmt,q_fmt", [("i8", "f16"), ("fp8", "bf16")])
-def test_one_byte_head_dim_64_small_blocks(gpu_lib, kv_fmt, q_fmt):
-    """One-byte multi-head rows of head_dim 64 in 8-token blocks: every length
-    from 1 to 44 (each offset of the last block, up to six blocks), whole and
-    split contexts; with 16-token partitions 8 and 16 kv heads put two and
-    four kv heads in a workgroup."""
+def test_one_byte_head_dim_64(gpu_lib, kv_fmt, q_fmt, bs):
+    """One-byte multi-head rows of head_dim 64: every length from 1 to 44 (each
+    offset of the last block), whole and split contexts.  With 16-token (or
+    block-sized) partitions 8 and 16 kv heads put two and four kv heads in a
+    workgroup, whose load rows then cover two heads each; one kv head reads
+    half-line rows (and at 8-token blocks re-reads the block's rows)."""
     for hkv in (1, 8, 16):
-        wl = W.make_workload(2, seed=40 + hkv, num_seqs=44, num_heads=hkv, num_kv_heads=hkv,
+        wl = W.make_workload(2, seed=40 + hkv + bs, num_seqs=44, num_heads=hkv, num_kv_heads=hkv,
                              head_dim=64, kv_fmt=kv_fmt, q_fmt=q_fmt,
-                             ctx=("fixed", list(range(1, 45))), max_blocks=6, block_size=8,
-                             poison_unused=True)
+                             ctx=("fixed", list(range(1, 45))), max_blocks=-(-48 // bs),
+                             block_size=bs, poison_unused=True)
         ref = oracle_decode(wl)
-        for part in (0, 16):
+        for part in (0, max(bs, 16)):
             got = out_f64(gpu_decode(gpu_lib, wl, partition_size=part))
             assert_parity(got, ref, kv_fmt, q_fmt, with_output_rounding=True,
-                          label=f"{kv_fmt} Hkv={hkv} part={part}")
+                          label=f"{kv_fmt} bs={bs} Hkv={hkv} part={part}")
+
+
+@pytest.mark.parametrize("kv_fmt,q_fmt", [("fp8", "f16"), ("i8", "bf16")])
+def test_one_byte_head_dim_64_head_pairs_70b_shape(gpu_lib, kv_fmt, q_fmt):
+    """The 70B-shaped layer's heads at head_dim 64 with a one-byte cache: 32
+    sequences x 64 kv heads give four kv heads per workgroup, read two per
+    load row; ragged lengths, table padding and unread slots poisoned."""
+    rng = np.random.default_rng(64)
+    lens = [int(x) for x in rng.integers(1, 400, 32)]
+    wl = W.make_workload(3, seed=64, num_seqs=32, head_dim=64, kv_fmt=kv_fmt, q_fmt=q_fmt,
+                         ctx=("fixed", lens), max_blocks=26, poison_unused=True)
+    assert pkv_mod.decode_partition_size(32, 64, 64, 64, 16, 26) == 0
+    got = out_f64(gpu_decode(gpu_lib, wl))
+    ref = oracle_decode(wl)
+    assert_parity(got, ref, kv_fmt, q_fmt, with_output_rounding=True, label=f"{kv_fmt} D=64 pairs")
 
 
 @pytest.mark.parametrize("bs", [8, 32])
