@@ -20,7 +20,9 @@
 //   * the waves of a workgroup take the partition's blocks round-robin; a wave
 //     reads a block's K rows of its kv head with 16-byte loads, LPR lanes per
 //     row (a 256-byte fp16 row of head_dim 128 is 16 lanes), RPI rows per load
-//     instruction, IPB instructions per block of BS tokens, then the same for V;
+//     instruction, IPB instructions per block of BS tokens, then the same for V
+//     (one-byte rows of head_dim 64 are half a line: there a load row covers
+//     two neighbouring kv heads, HR = 2, each lane working for one of them);
 //   * each lane holds its E query elements (per head) in registers, the dot
 //     product is finished by a DPP butterfly across the LPR lanes of a row;
 //   * every row group of a wave (the lanes that share token rows) keeps its own
