@@ -541,13 +541,40 @@ __device__ __forceinline__ void gqa_decode_body(const DecodeArgs& a, int item, u
     int64_t oa, ob;
     offsets(0, oa, ob);
     gqa_load<KF, QF, D, kTwo>(r0, kbase, vbase, oa, ob, goff, second);
-    for (int k = 0; k < kend; ++k) {
-      gqa_stage(tile, r0, soff);
-      if (k + 1 < kend) {
-        offsets(k + 1, oa, ob);
-        gqa_load<KF, QF, D, kTwo>(r0, kbase, vbase, oa, ob, goff, second);
+    if constexpr (D == 64) {
+      // head_dim 64: a tile's rows are few bytes and its compute is short, so
+      // the next tile's loads alone cannot cover the memory latency; two
+      // register sets keep tiles k + 1 and k + 2 in flight.
+      GqaStage<KF, QF, D> r1;
+      if (1 < kend) {
+        offsets(1, oa, ob);
+        gqa_load<KF, QF, D, kTwo>(r1, kbase, vbase, oa, ob, goff, second);
       }
-      compute(k);
+      for (int k = 0; k < kend; k += 2) {
+        gqa_stage(tile, r0, soff);
+        if (k + 2 < kend) {
+          offsets(k + 2, oa, ob);
+          gqa_load<KF, QF, D, kTwo>(r0, kbase, vbase, oa, ob, goff, second);
+        }
+        compute(k);
+        if (k + 1 < kend) {
+          gqa_stage(tile, r1, soff);
+          if (k + 3 < kend) {
+            offsets(k + 3, oa, ob);
+            gqa_load<KF, QF, D, kTwo>(r1, kbase, vbase, oa, ob, goff, second);
+          }
+          compute(k + 1);
+        }
+      }
+    } else {
+      for (int k = 0; k < kend; ++k) {
+        gqa_stage(tile, r0, soff);
+        if (k + 1 < kend) {
+          offsets(k + 1, oa, ob);
+          gqa_load<KF, QF, D, kTwo>(r0, kbase, vbase, oa, ob, goff, second);
+        }
+        compute(k);
+      }
     }
   }
   __syncthreads();  // the staging tiles become the merge buffer
