@@ -124,3 +124,30 @@ def test_random_cache_write_bit_exact(gpu_lib, k):
                                       wl.v_scales)
     np.testing.assert_array_equal(to_host(dev["key_cache"], kv_fmt), kref)
     np.testing.assert_array_equal(to_host(dev["value_cache"], kv_fmt), vref)
+
+
+@pytest.mark.parametrize("k", range(24))
+def test_random_long_context_parity(gpu_lib, k):
+    """Long contexts (up to 12000 tokens) on small grids, automatic
+    partitioning: a few (sequence, kv head) pairs split into hundreds of
+    partitions (the merge then takes several passes of its lanes), optional
+    long sliding windows."""
+    from test_gpu_decode import _behind_window
+    rng = np.random.default_rng(13000 + k)
+    kv_fmt, q_fmt = FORMATS[rng.integers(len(FORMATS))]
+    bs = int(rng.choice([8, 16, 32]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    kv_heads = int(rng.integers(1, 3))
+    num_seqs = int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.integers(2000, 12001, num_seqs)]
+    window = int(rng.integers(500, 9000)) if rng.random() < 0.4 else 0
+    wl = W.make_workload(2, seed=700 + k, num_seqs=num_seqs, num_heads=group * kv_heads,
+                         num_kv_heads=kv_heads, head_dim=int(rng.choice([64, 128])),
+                         kv_fmt=kv_fmt, q_fmt=q_fmt, ctx=("fixed", lens),
+                         max_blocks=-(-12000 // bs) + 1, block_size=bs, poison_unused=True)
+    if window:
+        wl = _behind_window(wl, window)
+    ref = oracle_decode(wl, window=window)
+    got = out_f64(gpu_decode(gpu_lib, wl, window=window))
+    assert_parity(got, ref, kv_fmt, q_fmt, with_output_rounding=True,
+                  label=f"{kv_fmt}/{q_fmt} bs={bs} G={group} Hkv={kv_heads} lens={lens} W={window}")
