@@ -151,3 +151,46 @@ def test_random_long_context_parity(gpu_lib, k):
     got = out_f64(gpu_decode(gpu_lib, wl, window=window))
     assert_parity(got, ref, kv_fmt, q_fmt, with_output_rounding=True,
                   label=f"{kv_fmt}/{q_fmt} bs={bs} G={group} Hkv={kv_heads} lens={lens} W={window}")
+
+
+@pytest.mark.parametrize("k", range(20))
+def test_random_block_copies_bit_exact(gpu_lib, k):
+    """copy_blocks on random pools and pair lists (distinct destinations, none
+    of them a source, repeated sources, more pairs than one launch takes),
+    with per-(block, kv head) scales for the one-byte formats: every byte of
+    the caches and scales equals a host copy."""
+    import torch
+    from gpu_util import DEV
+    rng = np.random.default_rng(15000 + k)
+    eb = int(rng.choice([1, 2, 4]))
+    scaled = eb == 1
+    nb = int(rng.integers(8, 900))
+    bs = int(rng.choice([8, 16, 32]))
+    hkv = int(rng.integers(1, 9))
+    d = int(rng.choice([64, 128]))
+    shape = (nb, bs, hkv, d * eb)
+    kc = rng.integers(0, 256, shape, dtype=np.uint8)
+    vc = rng.integers(0, 256, shape, dtype=np.uint8)
+    perm = rng.permutation(nb)
+    n_src = int(rng.integers(1, nb // 2 + 1))
+    srcs, free = perm[:n_src], perm[n_src:]
+    n_pairs = int(rng.integers(1, len(free) + 1))
+    dsts = free[:n_pairs]
+    pairs = [(int(rng.choice(srcs)), int(dd)) for dd in dsts]
+    dk, dv = torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV)
+    ks = vs = dks = dvs = None
+    if scaled:
+        ks = rng.uniform(0.001, 0.1, (nb, hkv)).astype(np.float32)
+        vs = rng.uniform(0.001, 0.1, (nb, hkv)).astype(np.float32)
+        dks, dvs = torch.from_numpy(ks).to(DEV), torch.from_numpy(vs).to(DEV)
+    gpu_lib.copy_blocks(dk, dv, pairs, dks, dvs)
+    torch.cuda.synchronize()
+    for s_, d_ in pairs:
+        kc[d_], vc[d_] = kc[s_], vc[s_]
+        if scaled:
+            ks[d_], vs[d_] = ks[s_], vs[s_]
+    np.testing.assert_array_equal(dk.cpu().numpy(), kc)
+    np.testing.assert_array_equal(dv.cpu().numpy(), vc)
+    if scaled:
+        np.testing.assert_array_equal(dks.cpu().numpy(), ks)
+        np.testing.assert_array_equal(dvs.cpu().numpy(), vs)
