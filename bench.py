@@ -28,6 +28,15 @@ reason.  ``read_probe_gbps`` is the library's read-only streaming probe
 this GPU.  ``cpu_baseline`` times the CPU
 oracle (test infrastructure, fp64 NumPy) on a bounded sample of the same
 workload on this host.
+
+After the timed steps the decode call alone is timed ``--sweep-calls`` times
+(100) from cold caches (a 512 MiB fill before each call, outside the HIP
+events): its median, p10 and p90 go into ``roofline``; ``parity`` compares
+every sequence of the batch with the oracle.  ``configs`` then holds the same
+statistics, algorithmic bytes, fraction of the HBM peak, context tokens/s,
+token x heads/s and whole-batch parity for every configuration in
+``--sweep-configs`` (default all eight; the headline's entry reuses its own
+numbers).
 """
 import argparse
 import hashlib
@@ -154,6 +163,121 @@ def cpu_baseline(wl, budget_s):
                       f"{wl.num_seqs} sequences, {tokens} context tokens), cache write + decode "
                       f"per sequence, fp64 NumPy, BLAS threads limited to {cores}",
             "seconds": round(spent, 3)}
+
+
+def parity_all(wl, out):
+    """Max abs error of the whole output against the oracle (every sequence and
+    head), the oracle's seconds, and the number of sequences."""
+    import oracle.paged_attention as pa
+    t = time.perf_counter()
+    ref = pa.paged_decode(wl.q, wl.q_fmt, wl.key_cache, wl.value_cache, wl.kv_fmt, wl.block_tables,
+                          wl.context_lens, wl.block_size, wl.scale, wl.k_scales, wl.v_scales,
+                          window=wl.window)
+    got = out.float().cpu().numpy().astype(np.float64)
+    return float(np.abs(got - ref).max()), time.perf_counter() - t
+
+
+def cold_call_times(torch, fn, calls, warmup, flush):
+    """Durations (us) of `calls` calls of fn from HIP events on the current
+    stream, each after filling `flush` (outside the events), so every call
+    starts with cold L2 and MALL."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(calls)]
+    for e0, e1 in ev:
+        flush.fill_(1)
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+
+
+def time_stats(us, ab, wl, num_heads):
+    """Median / p10 / p90 of the call durations with the rates they give."""
+    med = float(np.median(us))
+    tokens = ab["logical_tokens"]
+    return {"calls": int(len(us)), "decode_us_median": med,
+            "decode_us_p10": float(np.percentile(us, 10)),
+            "decode_us_p90": float(np.percentile(us, 90)), "decode_us_mean": float(np.mean(us)),
+            "algorithmic_bytes": ab["total"], "achieved_gbps": ab["total"] / (med * 1e-6) / 1e9,
+            "frac_of_hbm_peak": ab["total"] / (med * 1e-6) / 1e9 / HBM_PEAK_GBPS,
+            "context_tokens_per_s": tokens / (med * 1e-6),
+            "token_heads_per_s": tokens * num_heads / (med * 1e-6)}
+
+
+def config_sweep(args, torch, pkv, W, log, indices, flush, headline=None):
+    """Every listed configuration decoded `args.sweep_calls` times from cold
+    caches (HIP events; the shared-prompt workload on its shared-prefix path),
+    with the whole batch checked against the oracle.  `headline` = (index,
+    stats, parity) of the configuration already measured."""
+    rows = {}
+    for idx in indices:
+        if headline and idx == headline[0]:
+            rows[W.CONFIG_NAMES[idx]] = headline[1]
+            continue
+        t0 = time.perf_counter()
+        wl = W.make_workload(idx)
+        dev = torch.device("cuda:0")
+
+        def up(arr, fmt):
+            arr = np.ascontiguousarray(arr)
+            if fmt == "bf16":
+                return torch.from_numpy(arr.view(np.int16)).to(dev).view(torch.bfloat16)
+            if fmt == "fp8":
+                return torch.from_numpy(arr.view(np.uint8)).to(dev).view(torch.float8_e4m3fn)
+            return torch.from_numpy(arr).to(dev)
+
+        q = up(wl.q, wl.q_fmt)
+        kc, vc = up(wl.key_cache, wl.kv_fmt), up(wl.value_cache, wl.kv_fmt)
+        tables, lens = up(wl.block_tables, "i32"), up(wl.context_lens, "i32")
+        ks = up(wl.k_scales, "f32") if wl.kv_fmt in SCALED else None
+        vs = up(wl.v_scales, "f32") if wl.kv_fmt in SCALED else None
+        out = torch.empty_like(q)
+        B, H, D = q.shape
+        MB = tables.shape[1]
+        groups = None
+        if wl.shared_prefix_blocks and not wl.window:
+            groups = pkv.find_shared_prefixes(wl.block_tables, wl.context_lens, wl.block_size)
+            need = pkv.decode_prefix_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB,
+                                                    groups)
+            plens = torch.full((B,), groups[0][2], dtype=torch.int32, device=dev)
+        else:
+            need = pkv.decode_workspace_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, 0,
+                                             wl.window)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+        def decode():
+            if groups:
+                pkv.paged_attention_decode_prefix(out, q, kc, vc, tables, lens, wl.block_size,
+                                                  wl.scale, groups, ks, vs, workspace=ws,
+                                                  prefix_lens=plens)
+            else:
+                pkv.paged_attention_decode(out, q, kc, vc, tables, lens, wl.block_size, wl.scale,
+                                           ks, vs, workspace=ws, window=wl.window)
+
+        us = cold_call_times(torch, decode, args.sweep_calls, 10, flush)
+        ab = algorithmic_bytes(wl)
+        row = time_stats(us, ab, wl, H)
+        part = pkv.decode_partition_size(B, H, wl.num_kv_heads, D, wl.block_size, MB, 0, wl.window)
+        row["kernel"] = decode_kernel_names(wl, part, bool(groups))
+        row["decode_path"] = "shared-prefix" if groups else "per-sequence"
+        if ab["unique_tokens"] != ab["logical_tokens"]:
+            row["logical_bytes"] = ab["total"] - ab["kv"] + ab["logical_kv"]
+        err, osec = parity_all(wl, out)
+        tol = TOL[wl.kv_fmt]
+        row["parity"] = {"max_abs_err": err, "tol": tol, "seqs": "all", "num_seqs": B,
+                         "ok": err <= tol, "oracle_s": round(osec, 2)}
+        rows[wl.name] = row
+        log(f"config {idx} {wl.name}: median {row['decode_us_median']:.1f} us (p10 "
+            f"{row['decode_us_p10']:.1f}, p90 {row['decode_us_p90']:.1f}), "
+            f"{row['frac_of_hbm_peak']:.1%} of HBM peak, parity {err:.3g} on all {B} sequences "
+            f"({time.perf_counter() - t0:.1f}s)")
+        del q, kc, vc, tables, lens, ks, vs, out, ws
+        torch.cuda.empty_cache()
+    return rows
 
 
 def parity_sample(wl, out, n=4, seed=0):
@@ -477,6 +601,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--sweep-configs", default="1,2,3,4,5,6,7,8",
+                    help="configurations measured after the headline (cold-cache median / p10 / "
+                         "p90 of --sweep-calls decode calls, whole-batch parity); '' for none")
+    ap.add_argument("--sweep-calls", type=int, default=100)
     ap.add_argument("--swap", action="store_true",
                     help="measure preemption instead: swap-out/in over PCIe and batched CoW copies")
     ap.add_argument("--block-size-sweep", action="store_true",
@@ -671,8 +799,19 @@ def main():
     if ab["unique_tokens"] != ab["logical_tokens"]:
         result["roofline"]["logical_bytes_per_call"] = ab["total"] - ab["kv"] + ab["logical_kv"]
         result["roofline"]["logical_gbps"] = (ab["total"] - ab["kv"] + ab["logical_kv"]) / (decode_us * 1e-6) / 1e9
+    # The decode call alone from cold caches, many times: median and spread.
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    cold = time_stats(cold_call_times(torch, decode, args.sweep_calls, 10, flush), ab, wl, H)
+    cold["kernel"] = result["roofline"]["kernel"]
+    cold["decode_path"] = result["config"]["decode_path"]
+    result["roofline"].update({k: cold[k] for k in ("decode_us_median", "decode_us_p10",
+                                                     "decode_us_p90")})
+    result["roofline"]["cold_calls"] = cold["calls"]
+    result["token_heads_per_s"] = cold["token_heads_per_s"]
+    log(f"cold calls: median {cold['decode_us_median']:.1f} us, p10 {cold['decode_us_p10']:.1f}, "
+        f"p90 {cold['decode_us_p90']:.1f}")
     if not args.no_parity:
-        # one more step, then compare sampled sequences with the oracle
+        # one more step, then compare every sequence with the oracle
         write()
         decode()
         torch.cuda.synchronize()
@@ -680,11 +819,20 @@ def main():
         pa.reshape_and_cache(wl.k_new, wl.v_new, wl.new_fmt, wl.key_cache, wl.value_cache,
                              wl.kv_fmt, wl.slot_mapping, wl.block_size, wl.k_scales, wl.v_scales,
                              in_place=True)
-        err, seqs = parity_sample(wl, out)
+        err, osec = parity_all(wl, out)
         tol = TOL[wl.kv_fmt]
-        result["parity"] = {"max_abs_err": err, "tol": tol, "seqs": seqs, "ok": err <= tol}
-        log(f"parity on seqs {seqs}: max abs err {err:.3g} (tol {tol:g})")
+        result["parity"] = {"max_abs_err": err, "tol": tol, "seqs": "all", "num_seqs": B,
+                            "ok": err <= tol}
+        cold["parity"] = dict(result["parity"], oracle_s=round(osec, 2))
+        log(f"parity on all {B} sequences: max abs err {err:.3g} (tol {tol:g}, oracle {osec:.1f}s)")
         # the oracle leg below reads the caches as written (idempotent rewrite)
+    sweep = [int(x) for x in args.sweep_configs.split(",") if x.strip()]
+    if sweep:
+        del sets, kc, vc, ks, vs
+        torch.cuda.empty_cache()
+        result["configs"] = config_sweep(args, torch, pkv, W, log, sweep, flush,
+                                         headline=(args.config, cold) if args.seed is None else None)
+    del flush
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for about {args.cpu_budget:.0f}s")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -93,13 +93,36 @@ int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
 
 /*
  * Workspace bytes the decode needs for these shapes (0 when the context is
- * not split, in which case `workspace` may be NULL).  Same arguments as
- * pkv_decode_partition_size.
+ * not split, in which case `workspace` may be NULL): fp32 (max, sum) and
+ * head_dim accumulators per (sequence, query head, partition), the partial
+ * softmax results that the merge kernel combines.  The pages' kernel sketch
+ * ([P1] "PagedAttention注意力计算流程") has no split; the partials are this
+ * library's way to spread one long context over many workgroups.  Same
+ * arguments as pkv_decode_partition_size.
  */
 size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
                                  int head_dim, int block_size,
                                  int max_blocks_per_seq, int partition_size,
                                  int sliding_window);
+
+/*
+ * How pkv_paged_attention_decode will run for these shapes and this cache
+ * format (the same arguments, plus kv_dtype): the grid that splits the work
+ * of [P1] "PagedAttention注意力计算流程" into workgroups.  plan: host int[5]
+ * receiving
+ *   [0] tokens per partition (0 when contexts are not split),
+ *   [1] partitions per (sequence, kv head),
+ *   [2] kv heads per workgroup (multi-head kernel: 1, 2 or 4; else 1),
+ *   [3] kernel: 0 = multi-head kernel on the vector ALUs (one query head per
+ *       kv head, or an fp32 cache), 1 = grouped-query kernel on the matrix
+ *       cores,
+ *   [4] workgroups of the decode launch.
+ * Depends on shapes only, never on device data.  Errors: INVALID_ARG (bad
+ * shape, partition size or format), UNSUPPORTED (block size).
+ */
+int pkv_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, int partition_size, int sliding_window, int kv_dtype,
+                    int* plan);
 
 /*
  * Paged-attention decode ([P1] "PagedAttention注意力计算流程" and its kernel
@@ -118,16 +141,24 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  * ceil(n / bs) and slots past n are never read.
  *
  * With sliding_window = W > 0 only tokens max(0, n - W) .. n - 1 are attended
- * ([P2] "Sliding Window Attention控制长序列显存": only the most recent W
- * tokens' KV is kept); table entries of blocks before the window are never
- * read (they may be -1 after pkv_seq_trim_window).
+ * (the window of [P2] "Sliding Window Attention控制长序列显存"); table entries
+ * of blocks before the window are never read (they may be -1 after
+ * pkv_seq_trim_window).
  *
  *   out          device, [B][H][D] in q_dtype (written)
  *   q            device, [B][H][D] in q_dtype: F32, F16 or BF16
  *   key_cache    device, see layout above, kv_dtype
  *   value_cache  device, same shape and format as key_cache
  *   k_scales     device fp32 [NB][Hkv], required iff kv_dtype is I8 or FP8
- *   v_scales     device fp32 [NB][Hkv], required iff kv_dtype is I8 or FP8
+ *   v_scales     device fp32 [NB][Hkv], required iff kv_dtype is I8 or FP8.
+ *                Bound: with an F16 query and several query heads per kv head
+ *                (the matrix-core kernel, here and in the shared-prefix
+ *                decode) each softmax weight, up to 2^8, is multiplied by its
+ *                block's v_scale and fed to the matrix cores as two f16 parts;
+ *                v_scale <= 256 keeps that product within about 22 bits of
+ *                precision.  Larger values lose precision, and above 511 the
+ *                parts saturate (wrong outputs).  Scales are device data and
+ *                are not checked.  BF16 queries have no such bound.
  *   block_tables device int32 [B][max_blocks_per_seq]
  *   context_lens device int32 [B]; values are clamped to
  *                [0, max_blocks_per_seq * block_size]
@@ -341,13 +372,17 @@ int pkv_incref(pkv_allocator* a, const int32_t* ids, int n);
  * INVALID_ARG if the block is not allocated; OOM if no block is free. */
 int pkv_copy_on_write(pkv_allocator* a, int32_t id, int32_t* new_id, int* copied);
 
+/* Reference count of a block, and the number of free blocks ([P3] section 二:
+ * the block manager's per-block counts and its free list). */
 int pkv_ref_count(const pkv_allocator* a, int32_t id, int* out);
 int pkv_num_free(const pkv_allocator* a, int* out);
 /* 1 - free / num_blocks ([P3] section 二, usage_ratio). */
 int pkv_usage_ratio(const pkv_allocator* a, double* out);
-/* Copy of the free list, bottom to top (the next block to leave is last). */
+/* Copy of the free list ([P3] section 二), bottom to top (the next block to
+ * leave is last). */
 int pkv_free_list(const pkv_allocator* a, int32_t* out, int cap, int* n);
-/* Number of copy-on-write copies handed out so far. */
+/* Number of copy-on-write copies handed out so far ([P3] section 二,
+ * copy_on_write). */
 int pkv_cow_count(const pkv_allocator* a, int64_t* out);
 
 /* Sequences: a logical block table plus a token count ([P3] BlockTable). */
@@ -367,8 +402,8 @@ int pkv_seq_fork(pkv_allocator* a, int32_t seq, int32_t* child);
 int pkv_seq_append_tokens(pkv_allocator* a, int32_t seq, int n, int32_t* slots_out,
                           int32_t* cow_pairs_out, int cow_cap, int* n_cow);
 /*
- * Sliding window ([P2] "Sliding Window Attention控制长序列显存": only the most
- * recent W tokens' KV is kept, so a sequence's cache stays constant in size):
+ * Sliding window ([P2] "Sliding Window Attention控制长序列显存": a sequence
+ * keeps the KV of its last W tokens only, so its cache stays bounded in size):
  * drop this sequence's reference to every block that holds no token of its
  * last `window` tokens (blocks before the one holding token
  * max(0, tokens - window)).  Their table entries become -1 (exported as the
@@ -423,7 +458,11 @@ int pkv_seq_block_ids(const pkv_allocator* a, int32_t seq, int32_t* out, int cap
  * token's logical block has not been allocated; INVALID_ARG if swapped out. */
 int pkv_seq_physical_block(const pkv_allocator* a, int32_t seq, int token, int32_t* out);
 /*
- * Export host block tables for a batch: out_tables int32[n][max_blocks]
+ * Export host block tables for a batch, in the layout the decode reads: one
+ * row of max_blocks entries per sequence (the row stride max_blocks of the
+ * table lookup in the kernel sketch of [P1] "PagedAttention注意力计算流程"),
+ * filled from the sequences' logical tables ([P3] section 二, BlockTable).
+ * out_tables int32[n][max_blocks]
  * padded with `pad`, out_lens int32[n] token counts.  INVALID_ARG if a
  * sequence holds more than max_blocks blocks.
  */

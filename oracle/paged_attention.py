@@ -114,9 +114,9 @@ def paged_decode(q, q_fmt, key_cache, value_cache, kv_fmt, block_tables,
     key_cache    [NB, block_size, Hkv, D] in ``kv_fmt``; value_cache likewise
     block_tables [B, MB] int, context_lens [B] int
     k_scales, v_scales [NB, Hkv] fp32 (``kv_fmt`` "i8" or "fp8" only)
-    window       0, or the sliding window W: only the last W tokens of each
-                 context are attended to ([P2] "Sliding Window Attention控制
-                 长序列显存": only the most recent W tokens' KV is kept)
+    window       0, or the sliding window W of [P2] "Sliding Window
+                 Attention控制长序列显存": positions max(0, n - W) .. n - 1 of a
+                 context of n tokens are attended to
 
     For each sequence s and query head h: gather the attended keys and values
     through the table (the first ctx[s] tokens, or the last W of them), score

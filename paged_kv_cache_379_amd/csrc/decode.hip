@@ -255,6 +255,41 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, 
   return static_cast<size_t>(num_seqs) * num_heads * parts * (head_dim + 2) * sizeof(float);
 }
 
+int pkv_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
+                    int max_blocks_per_seq, int partition_size, int sliding_window, int kv_dtype,
+                    int* plan) {
+  PKV_API_BEGIN
+  if (!plan) return pkv::fail(PKV_ERR_INVALID_ARG, "NULL plan");
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq) ||
+      num_seqs == 0 || sliding_window < 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "bad shape");
+  if (!pkv_dev::supported_block_size(block_size))
+    return pkv::fail(PKV_ERR_UNSUPPORTED, "block_size %d (8, 16 or 32)", block_size);
+  if (kv_dtype < PKV_F32 || kv_dtype > PKV_FP8)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "kv_dtype %d", kv_dtype);
+  if (static_cast<int64_t>(max_blocks_per_seq) * block_size > INT32_MAX / 2)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  const int64_t span = attended_tokens(max_blocks_per_seq, block_size, sliding_window);
+  const int64_t pt = partition_tokens(num_seqs, num_kv_heads, span, block_size, partition_size,
+                                      window_binds(max_blocks_per_seq, block_size, sliding_window));
+  if (pt <= 0)
+    return pkv::fail(PKV_ERR_INVALID_ARG, "partition_size %d is not a multiple of %d tokens",
+                     partition_size, pkv_dev::partition_align(block_size));
+  const int parts = static_cast<int>((span + pt - 1) / pt);
+  const int group = num_heads / num_kv_heads;
+  const bool vector = kv_dtype == PKV_F32 || group == 1;
+  const int hpi = vector ? mha_heads_per_item(num_seqs, num_heads, num_kv_heads, parts, kv_dtype) : 1;
+  const int64_t items = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpi) * parts;
+  if (items > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "grid too large");
+  plan[0] = parts > 1 ? static_cast<int>(pt) : 0;
+  plan[1] = parts;
+  plan[2] = hpi;
+  plan[3] = vector ? 0 : 1;
+  plan[4] = static_cast<int>(items);
+  return PKV_OK;
+  PKV_API_END
+}
+
 int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
                                const void* value_cache, const float* k_scales,
                                const float* v_scales, const int32_t* block_tables,

@@ -111,7 +111,10 @@ __device__ __forceinline__ Span attended_span(const DecodeArgs& a, int seq) {
   int first = a.window > 0 ? max(0, ctx - a.window) : 0;
   int nchunks = 0;
   if (a.prefix_lens) {
-    const int pl = min(max(a.prefix_lens[seq], 0), ctx);
+    // at most the part_base chunk slots the workspace holds, whatever the
+    // device value says (a value that disagrees with the groups gives a wrong
+    // output, never a read outside the workspace)
+    const int pl = min(min(max(a.prefix_lens[seq], 0), ctx), a.part_base * a.prefix_chunk);
     first = max(first, pl);
     nchunks = (pl + a.prefix_chunk - 1) / a.prefix_chunk;
   }

@@ -27,4 +27,4 @@ void clear_error() { g_last_error.clear(); }
 
 extern "C" const char* pkv_last_error(void) { return g_last_error.c_str(); }
 
-extern "C" int pkv_abi_version(void) { return 3; }
+extern "C" int pkv_abi_version(void) { return 4; }

@@ -351,7 +351,7 @@ def pin_cache_write_int8(pa):
 
 def pin_window_equals_contiguous_tail(pa):
     """Sliding window W: paged decode == torch SDPA on the contiguous last W
-    tokens ([P2] sliding window: only the most recent W tokens take part),
+    tokens (the window of [P2] "Sliding Window Attention控制长序列显存"),
     for windows below, at and across block boundaries and past the context."""
     rng = np.random.default_rng(23)
     h, hkv, d = 4, 2, 32
@@ -392,7 +392,7 @@ def pin_window_one_and_released_blocks(pa):
     assert np.array_equal(one[0], vc.reshape(-1, hkv, d)[last].astype(np.float64))
     released = alloc.seq_trim_window(sid, w)
     assert released and all(0 <= b < 12 for b in released)
-    assert sum(1 for b in alloc.seqs[sid]["blocks"] if b >= 0) <= (w + BS - 1) // BS + 1
+    assert sum(1 for b in alloc.table(sid) if b >= 0) <= (w + BS - 1) // BS + 1
     kp, vp = kc.copy(), vc.copy()
     for slot in slots[: n - w]:
         kp.reshape(-1, hkv, d)[slot] = np.nan

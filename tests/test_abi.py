@@ -27,7 +27,7 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert hasattr(lib, name), f"{name} declared in pkv.h but not exported"
     # the binding wraps exactly the declared set
     assert sorted(pkv.EXPORTED) == names
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
 
 
 def _header_params():
@@ -280,3 +280,30 @@ def test_binding_rejects_unsupported_dtypes():
     for dt, want in ((torch.float16, pkv.F16), (torch.bfloat16, pkv.BF16), (torch.int8, pkv.I8),
                      (torch.float8_e4m3fn, pkv.FP8), (torch.float32, pkv.F32)):
         assert pkv._fmt(torch.zeros(1, dtype=dt)) == want
+
+
+def test_decode_plan_reports_the_launch():
+    """The plan query names the kernel and the split the decode uses; its
+    partition size and workspace agree with the two sizing calls."""
+    p = pkv.decode_plan(32, 64, 64, 128, 16, 128, pkv.F16)            # 70B-shaped fp16
+    assert p == {"partition_tokens": 0, "partitions": 1, "kv_heads_per_workgroup": 2,
+                 "kernel": "multi_head", "workgroups": 32 * 32}
+    p = pkv.decode_plan(32, 64, 64, 128, 16, 128, pkv.FP8)            # one-byte: four heads
+    assert p["kv_heads_per_workgroup"] == 4 and p["workgroups"] == 32 * 16
+    assert pkv.decode_plan(16, 64, 64, 128, 16, 4, pkv.I8)["kv_heads_per_workgroup"] == 2
+    assert pkv.decode_plan(4, 64, 64, 128, 16, 4, pkv.I8)["kv_heads_per_workgroup"] == 1
+    assert pkv.decode_plan(32, 32, 32, 128, 16, 128, pkv.F16)["kv_heads_per_workgroup"] == 1
+    p = pkv.decode_plan(256, 32, 8, 128, 16, 256, pkv.I8)             # grouped-query, split
+    assert p["kernel"] == "grouped_query" and p["kv_heads_per_workgroup"] == 1
+    assert p["partition_tokens"] == pkv.decode_partition_size(256, 32, 8, 128, 16, 256) == 1024
+    assert p["partitions"] == 4 and p["workgroups"] == 256 * 8 * 4
+    assert pkv.decode_plan(2, 8, 2, 64, 16, 7, pkv.F32)["kernel"] == "multi_head"
+    p = pkv.decode_plan(4, 8, 8, 128, 16, 20, pkv.F16, partition_size=64)
+    assert (p["partition_tokens"], p["partitions"]) == (64, 5)
+    for bad in (dict(partition_size=24), dict(kv_dtype=9)):
+        args = dict(kv_dtype=pkv.F16, partition_size=0)
+        args.update(bad)
+        with pytest.raises(ValueError):
+            pkv.decode_plan(4, 8, 8, 128, 16, 20, args["kv_dtype"], args["partition_size"])
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_plan(4, 8, 8, 128, 12, 20, pkv.F16)                 # block size 12

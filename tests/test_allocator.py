@@ -125,8 +125,8 @@ def test_differential_against_model(seed):
             op = ["free", "incref"][int(rng.integers(2))]
             if op == "free":
                 # never free blocks a live sequence still owns through its table
-                owned = {b for s in live for b in model.seqs[s]["blocks"]
-                         if b >= 0 and not model.seqs[s]["swapped"]}
+                owned = {b for s in live for b in model.table(s)
+                         if b >= 0 and not model.seq_is_swapped(s)}
                 ids = [i for i in ids if i not in owned] or [nb + 5]
             a, b = _apply(model, op, (ids,)), _apply(lib, op, (ids,))
             assert a[0] == b[0], (step, op, ids, a, b)
@@ -159,18 +159,18 @@ def test_differential_against_model(seed):
             a, b = _apply(model, op, (sid,)), _apply(lib, op, (sid,))
             assert a == b, (step, op, a, b)
         for sid in live:
-            assert model.seqs[sid]["blocks"] == lib.seq_block_ids(sid)
+            assert model.table(sid) == lib.seq_block_ids(sid)
             assert model.seq_is_swapped(sid) == lib.seq_is_swapped(sid)
-        assert len(model.host_free) == lib.host_num_free()
-        assert model.ref_count == [lib.ref_count(i) for i in range(nb)]
-        assert model.free_blocks == lib.free_list()
+        assert len(model.host_free_order()) == lib.host_num_free()
+        assert model.ref_counts() == [lib.ref_count(i) for i in range(nb)]
+        assert model.free_order() == lib.free_list()
         assert model.usage_ratio() == pytest.approx(lib.usage_ratio())
     for sid in live:
         model.seq_free(sid)
         lib.seq_free(sid)
     assert all(lib.ref_count(i) == 0 for i in range(nb))
     assert sorted(lib.free_list()) == list(range(nb))
-    assert model.cow_copies == lib.cow_count()
+    assert model.cow_count() == lib.cow_count()
 
 
 def test_shared_prefix_config_refcounts():

@@ -50,19 +50,19 @@ def test_lifo_pop_from_end():
 def test_oom_all_or_nothing():
     a = AllocatorModel(4, 16)
     a.allocate(3)
-    before = (list(a.free_blocks), list(a.ref_count))
+    before = (a.free_order(), a.ref_counts())
     with pytest.raises(OutOfBlocks):
         a.allocate(2)
-    assert (a.free_blocks, a.ref_count) == before
+    assert (a.free_order(), a.ref_counts()) == before
 
 
 def test_double_free_leaves_state():
     a = AllocatorModel(4, 16)
     b = a.allocate(2)
-    before = (list(a.free_blocks), list(a.ref_count))
+    before = (a.free_order(), a.ref_counts())
     with pytest.raises(DoubleFree):
         a.free([b[0], b[0]])
-    assert (a.free_blocks, a.ref_count) == before
+    assert (a.free_order(), a.ref_counts()) == before
     a.free([b[0]])
     with pytest.raises(DoubleFree):
         a.free([b[0]])
@@ -75,9 +75,9 @@ def test_copy_on_write_semantics():
     a.incref([b])
     new, copied = a.copy_on_write(b)
     assert copied and new != b
-    assert a.ref_count[b] == 1 and a.ref_count[new] == 1
+    assert a.refs(b) == 1 and a.refs(new) == 1
     with pytest.raises(ValueError):
-        a.copy_on_write(a.free_blocks[0])          # unowned block
+        a.copy_on_write(a.free_order()[0])          # unowned block
 
 
 def test_fork_and_partial_block_cow():
@@ -86,8 +86,8 @@ def test_fork_and_partial_block_cow():
     parent = a.seq_create()
     a.seq_append_tokens(parent, 37)                # 2 full blocks + 5 tokens
     kids = [a.seq_fork(parent) for _ in range(3)]
-    shared = a.seqs[parent]["blocks"]
-    assert all(a.ref_count[b] == 4 for b in shared)
+    shared = a.table(parent)
+    assert all(a.refs(b) == 4 for b in shared)
     copies = []
     for sid in kids + [parent]:
         slots, cow = a.seq_append_tokens(sid, 1)
@@ -97,22 +97,22 @@ def test_fork_and_partial_block_cow():
     # writes in place
     assert [len(c) for c in copies] == [1, 1, 1, 0]
     assert all(c[0][0] == shared[2] for c in copies[:3])
-    assert a.ref_count[shared[2]] == 1
-    assert all(a.ref_count[b] == 4 for b in shared[:2])
+    assert a.refs(shared[2]) == 1
+    assert all(a.refs(b) == 4 for b in shared[:2])
     for sid in kids + [parent]:
         a.seq_free(sid)
-    assert not any(a.ref_count)
-    assert sorted(a.free_blocks) == list(range(32))
+    assert not any(a.ref_counts())
+    assert sorted(a.free_order()) == list(range(32))
 
 
 def test_append_all_or_nothing():
     a = AllocatorModel(3, 16)
     s = a.seq_create()
     a.seq_append_tokens(s, 40)                     # 3 blocks
-    before = (list(a.free_blocks), list(a.ref_count), dict(a.seqs[s]))
+    before = (a.free_order(), a.ref_counts(), a.table(s), a.length(s))
     with pytest.raises(OutOfBlocks):
         a.seq_append_tokens(s, 9)                  # needs a 4th block
-    assert (a.free_blocks, a.ref_count, a.seqs[s]) == (before[0], before[1], before[2])
+    assert (a.free_order(), a.ref_counts(), a.table(s), a.length(s)) == before
 
 
 def test_random_ops_invariants():
@@ -135,14 +135,14 @@ def test_random_ops_invariants():
             pass
         refs = np.zeros(64, int)
         for sid in live:
-            for b in a.seqs[sid]["blocks"]:
+            for b in a.table(sid):
                 refs[b] += 1
-        assert refs.tolist() == a.ref_count
-        assert sorted(a.free_blocks + [b for b in range(64) if refs[b]]) == list(range(64))
+        assert refs.tolist() == a.ref_counts()
+        assert sorted(a.free_order() + [b for b in range(64) if refs[b]]) == list(range(64))
     for sid in live:
         a.seq_free(sid)
-    assert not any(a.ref_count)
-    assert sorted(a.free_blocks) == list(range(64))
+    assert not any(a.ref_counts())
+    assert sorted(a.free_order()) == list(range(64))
 
 
 # ---------------------------------------------------------------------------
@@ -157,9 +157,9 @@ def _write_tokens(mem, slots, bs, values):
 
 
 def _gather(model, sid, mem):
-    seq = model.seqs[sid]
+    table = model.table(sid)
     bs = model.block_size
-    return [mem[seq["blocks"][t // bs]][t % bs] for t in range(seq["tokens"])]
+    return [mem[table[t // bs]][t % bs] for t in range(model.length(sid))]
 
 
 def pin_swap_round_trip_preserves_contents(cls):
@@ -183,7 +183,7 @@ def pin_swap_round_trip_preserves_contents(cls):
         host[h_] = dict(dev[d_])
     assert m.seq_is_swapped(c)
     n = m.seq_create()                      # another request takes the freed blocks
-    slots, _ = m.seq_append_tokens(n, len(m.free_blocks) * bs)
+    slots, _ = m.seq_append_tokens(n, len(m.free_order()) * bs)
     _write_tokens(dev, slots, bs, ["junk"] * len(slots))
     assert _gather(m, p, dev) == want_p
     m.seq_free(n)
@@ -193,7 +193,7 @@ def pin_swap_round_trip_preserves_contents(cls):
     assert _gather(m, c, dev) == want_c and _gather(m, p, dev) == want_p
     # it resumes: the next token lands after the restored ones
     slots, cow = m.seq_append_tokens(c, 1)
-    assert not cow and slots[0] // bs == m.seqs[c]["blocks"][-1]
+    assert not cow and slots[0] // bs == m.table(c)[-1]
 
 
 def pin_swap_conservation(cls):
@@ -226,22 +226,22 @@ def pin_swap_conservation(cls):
         refs = np.zeros(nb, int)
         held_host = []
         for sid in live:
-            ids = [b for b in m.seqs[sid]["blocks"] if b >= 0]
+            ids = [b for b in m.table(sid) if b >= 0]
             if m.seq_is_swapped(sid):
                 held_host += ids
             else:
                 np.add.at(refs, ids, 1)
-        assert refs.tolist() == m.ref_count
-        assert sorted(m.free_blocks + [b for b in range(nb) if refs[b]]) == list(range(nb))
-        assert sorted(m.host_free + held_host) == list(range(nhb))
+        assert refs.tolist() == m.ref_counts()
+        assert sorted(m.free_order() + [b for b in range(nb) if refs[b]]) == list(range(nb))
+        assert sorted(m.host_free_order() + held_host) == list(range(nhb))
     for sid in [s for s in live if m.seq_is_swapped(s)]:
         m.seq_free(sid)
         live.remove(sid)
-    assert sorted(m.host_free) == list(range(nhb))
+    assert sorted(m.host_free_order()) == list(range(nhb))
     m.set_host_pool(nb * 2)
     for sid in live:
         m.seq_swap_out(sid)
-    assert not any(m.ref_count) and sorted(m.free_blocks) == list(range(nb))
+    assert not any(m.ref_counts()) and sorted(m.free_order()) == list(range(nb))
 
 
 def pin_swap_all_or_nothing(cls):
@@ -249,10 +249,10 @@ def pin_swap_all_or_nothing(cls):
     m.set_host_pool(2)
     s = m.seq_create()
     m.seq_append_tokens(s, 12)
-    before = (list(m.seqs[s]["blocks"]), list(m.free_blocks), list(m.host_free))
+    before = (m.table(s), m.free_order(), m.host_free_order())
     with pytest.raises(OutOfBlocks):
         m.seq_swap_out(s)
-    assert (m.seqs[s]["blocks"], m.free_blocks, m.host_free) == before
+    assert (m.table(s), m.free_order(), m.host_free_order()) == before
     with pytest.raises(ValueError):
         m.seq_swap_in(s)
 
@@ -266,14 +266,14 @@ def test_swap_pins(pin):
 
 
 SWAP_MUTATIONS = {
-    "pairs_reversed": ("pairs.append((b, h))", "pairs.append((h, b))"),
-    "out_keeps_reference": ("            self.free([b])\n            seq[\"blocks\"][j] = h",
-                            "            seq[\"blocks\"][j] = h"),
-    "in_keeps_host_block": ("            self.host_free.append(h)\n", ""),
-    "in_pairs_reversed": ("pairs.append((h, d))", "pairs.append((d, h))"),
-    "out_not_all_or_nothing": ("        if len(held) > len(self.host_free):\n            raise OutOfBlocks(f\"need {len(held)} host blocks, {len(self.host_free)} free\")\n",
-                               ""),
-    "in_table_not_updated": ("            seq[\"blocks\"][j] = d\n", ""),
+    "pairs_reversed": ("out.append((dev, host))", "out.append((host, dev))"),
+    "out_keeps_reference": ("            self.free([dev])\n", ""),
+    "in_keeps_host_block": ("            self._host_stack.give_back(host)\n", ""),
+    "in_pairs_reversed": ("pairs.append((host, dev))", "pairs.append((dev, host))"),
+    "out_not_all_or_nothing": ("        if len(moving) > len(self._host_stack):\n"
+                               "            raise OutOfBlocks(f\"need {len(moving)} host blocks, "
+                               "{len(self._host_stack)} free\")\n", ""),
+    "in_table_not_updated": ("            seq.table[j] = dev\n", ""),
 }
 
 

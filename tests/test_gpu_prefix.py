@@ -160,7 +160,7 @@ def test_prefix_merged_in_the_decode_kernel(gpu_lib):
 
 def test_prefix_shared_prompt_configuration_full_size(gpu_lib):
     """The 64-sequence, 2000-token shared-prompt workload at full size in the
-    benchmark's launch configuration; sampled sequences against the oracle."""
+    benchmark's launch configuration; every sequence against the oracle."""
     from gpu_util import oracle_decode, upload
     from paged_kv_cache_379_amd import workloads as W
     pkv = gpu_lib
@@ -174,9 +174,8 @@ def test_prefix_shared_prompt_configuration_full_size(gpu_lib):
                                       wl.scale, groups)
     torch.cuda.synchronize()
     got = out_f64(out)
-    seqs = np.array([0, 17, 40, 63])
-    assert_parity(got[seqs], oracle_decode(wl, seqs), "bf16", label="shared prompt full size")
-    assert np.isfinite(got).all()
+    err = assert_parity(got, oracle_decode(wl), "bf16", label="shared prompt full size")
+    print(f"shared prompt full size: all {wl.num_seqs} sequences, max abs err {err:.3g}")
 
 
 @pytest.mark.parametrize("prefix", [8000, 16000])

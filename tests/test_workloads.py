@@ -42,7 +42,7 @@ def test_tables_match_allocator(index):
     if index == 4:
         shared = st["tables"][0, :125]
         assert st["prefix_blocks"] == 125          # 2000 = 125 * 16: no partial block
-        assert all(a.ref_count[b] == 64 for b in shared)
+        assert all(a.refs(b) == 64 for b in shared)
         assert (st["tables"][:, :125] == shared).all()
     else:
         used = np.concatenate([st["tables"][s, :(n + 15) // 16] for s, n in enumerate(st["lens"])])
