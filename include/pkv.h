@@ -192,6 +192,32 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_attention_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and result, without `workspace` and
+ * `workspace_bytes`.  When the contexts are split, the partials go to a
+ * scratch array of PKV_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds
+ * in each GPU's memory from its first call on that GPU until the process
+ * ends; the call itself allocates nothing.  Shapes whose
+ * pkv_decode_workspace_size exceeds that are rejected with WORKSPACE (nothing
+ * is launched).  Every call on one GPU shares that GPU's scratch: calls that
+ * may overlap on one GPU (other streams, other threads) race and must be
+ * ordered by the caller.  Nothing in the scratch has to start at zero (each
+ * call writes every partial it reads).  Errors: those of
+ * pkv_paged_attention_decode, plus HIP if the scratch's device address cannot
+ * be obtained.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* key_cache,
+                                       const void* value_cache, const float* k_scales,
+                                       const float* v_scales, const int32_t* block_tables,
+                                       const int32_t* context_lens, int num_seqs, int num_heads,
+                                       int num_kv_heads, int head_dim, int block_size,
+                                       int max_blocks_per_seq, int num_blocks, float scale,
+                                       int q_dtype, int kv_dtype, int partition_size,
+                                       int sliding_window, void* stream);
+
+/*
  * Shared-prefix decode ([P1] "vLLM调度器与PagedAttention协同工作" item 2:
  * requests that share a system prompt share its blocks; [P2] "Prefix Cache
  * 复用共享前缀的KV Cache"): the same result as pkv_paged_attention_decode,

@@ -17,6 +17,7 @@ import numpy as np
 __all__ = [
     "load", "LIB_PATH", "PkvError", "OutOfBlocks", "DoubleFree",
     "paged_attention_decode", "decode_workspace_size", "decode_partition_size", "decode_plan",
+    "paged_attention_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "paged_attention_decode_prefix", "decode_prefix_workspace_size", "find_shared_prefixes",
     "reshape_and_cache", "copy_blocks", "swap_blocks", "stream_copy", "stream_read",
     "validate_tables",
@@ -57,6 +58,8 @@ _SIGS = {
     "pkv_decode_plan": (_c_int, [_c_int] * 9 + [_i32p]),
     "pkv_paged_attention_decode": (_c_int, [_vp] * 8 + [_c_int] * 7 + [ctypes.c_float] + [_c_int] * 4
                                    + [_vp, _c_size, _vp]),
+    "pkv_paged_attention_decode_noalloc": (_c_int, [_vp] * 8 + [_c_int] * 7 + [ctypes.c_float]
+                                           + [_c_int] * 4 + [_vp]),
     "pkv_paged_attention_decode_prefix": (_c_int, [_vp] * 9 + [_c_int] * 7 + [ctypes.c_float]
                                           + [_c_int] * 2 + [_i32p, _c_int, _vp, _c_size, _vp]),
     "pkv_decode_prefix_workspace_size": (_c_size, [_c_int] * 6 + [_i32p, _c_int]),
@@ -252,6 +255,38 @@ def paged_attention_decode(out, q, key_cache, value_cache, block_tables, context
         _dev_ptr(context_lens, "context_lens", torch.int32),
         B, H, Hkv, D, bs, MB, NB, float(scale), _fmt(q), _fmt(key_cache), int(partition_size),
         int(window), _dev_ptr(workspace, "workspace"), ws_bytes, _stream(stream))
+    _check(rc)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # PKV_NOALLOC_SCRATCH_BYTES (include/pkv.h)
+
+
+def paged_attention_decode_noalloc(out, q, key_cache, value_cache, block_tables, context_lens,
+                                   block_size, scale, k_scales=None, v_scales=None,
+                                   partition_size=0, stream=None, window=0):
+    """:func:`paged_attention_decode` with the split-context partials in the
+    library's static per-GPU scratch (NOALLOC_SCRATCH_BYTES) instead of a
+    workspace: neither the library nor this binding allocates device memory.
+    Calls that may overlap on one GPU share that scratch and must be ordered."""
+    lib = load()
+    B, H, D = q.shape
+    NB, bs, Hkv, D2 = key_cache.shape
+    if D2 != D or bs != block_size or tuple(out.shape) != (B, H, D) or out.dtype != q.dtype:
+        raise ValueError("shape or dtype mismatch between q, out and the caches")
+    if tuple(value_cache.shape) != tuple(key_cache.shape) or value_cache.dtype != key_cache.dtype:
+        raise ValueError("value_cache must match key_cache")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B, MB] and context_lens [B]")
+    torch = _torch()
+    rc = lib.pkv_paged_attention_decode_noalloc(
+        _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(key_cache, "key_cache"),
+        _dev_ptr(value_cache, "value_cache"), _dev_ptr(k_scales, "k_scales", torch.float32),
+        _dev_ptr(v_scales, "v_scales", torch.float32),
+        _dev_ptr(block_tables, "block_tables", torch.int32),
+        _dev_ptr(context_lens, "context_lens", torch.int32),
+        B, H, Hkv, D, bs, block_tables.shape[1], NB, float(scale), _fmt(q), _fmt(key_cache),
+        int(partition_size), int(window), _stream(stream))
     _check(rc)
     return out
 

@@ -3,6 +3,7 @@
 // of partitions when the context is split).
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "decode_dispatch.h"
@@ -220,6 +221,40 @@ int plan_prefix(int num_seqs, int num_heads, int num_kv_heads, int block_size, i
   plan->part_tokens = static_cast<int>(pt);
   plan->parts = static_cast<int>((span + pt - 1) / pt);
   return PKV_OK;
+}
+
+// Scratch of pkv_paged_attention_decode_noalloc: the split-context partials
+// for callers that cannot allocate device memory.  Each GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` names
+// a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+struct ScratchAddress {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchAddress g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch, or NULL (with *err set).
+void* scratch_address(int* device, hipError_t* err) {
+  *err = hipGetDevice(device);
+  if (*err != hipSuccess) return nullptr;
+  if (*device < 0 || *device >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  ScratchAddress& slot = g_scratch[*device];
+  std::call_once(slot.once, [&slot] {
+    void* p = nullptr;
+    slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    slot.ptr = slot.err == hipSuccess ? p : nullptr;
+  });
+  *err = slot.err;
+  return slot.ptr;
 }
 
 }  // namespace
@@ -544,6 +579,42 @@ int pkv_paged_attention_decode_prefix(void* out, const void* q, const void* key_
       return pkv::fail(PKV_ERR_HIP, "partition merge launch: %s", hipGetErrorString(err));
   }
   return PKV_OK;
+  PKV_API_END
+}
+
+int pkv_paged_attention_decode_noalloc(void* out, const void* q, const void* key_cache,
+                                       const void* value_cache, const float* k_scales,
+                                       const float* v_scales, const int32_t* block_tables,
+                                       const int32_t* context_lens, int num_seqs, int num_heads,
+                                       int num_kv_heads, int head_dim, int block_size,
+                                       int max_blocks_per_seq, int num_blocks, float scale,
+                                       int q_dtype, int kv_dtype, int partition_size,
+                                       int sliding_window, void* stream) {
+  PKV_API_BEGIN
+  if (!shapes_ok(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq))
+    return pkv::fail(PKV_ERR_INVALID_ARG, "bad shape");
+  const size_t need =
+      pkv_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                max_blocks_per_seq, partition_size, sliding_window);
+  if (need > kScratchBytes)
+    return pkv::fail(PKV_ERR_WORKSPACE,
+                     "these shapes need %zu bytes of partials; the static scratch holds %zu "
+                     "(use pkv_paged_attention_decode with a workspace)",
+                     need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    int device = -1;
+    hipError_t err = hipSuccess;
+    ws = scratch_address(&device, &err);
+    if (!ws)
+      return pkv::fail(PKV_ERR_HIP, "scratch address on device %d: %s", device,
+                       hipGetErrorString(err));
+  }
+  return pkv_paged_attention_decode(out, q, key_cache, value_cache, k_scales, v_scales,
+                                    block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                                    head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                                    q_dtype, kv_dtype, partition_size, sliding_window, ws,
+                                    need > 0 ? kScratchBytes : 0, stream);
   PKV_API_END
 }
 
