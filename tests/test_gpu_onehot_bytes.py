@@ -55,6 +55,13 @@ def _pow2_code(k, fmt):
     return np.int8(1 << k) if fmt == "i8" else np.uint8((k + 7) << 3)
 
 
+def _unsigned_zero(bits):
+    """Output bits with -0 read as +0 (the two zeros are the same value; a sum
+    that starts at +0 may end at either when its terms are zeros of both
+    signs)."""
+    return np.where(bits == 0x8000, np.uint16(0), bits)
+
+
 def _out_bits(x, fmt):
     """float32 values -> output-format bits (round to nearest even)."""
     x = np.asarray(x, np.float32)
@@ -147,7 +154,7 @@ class Probe:
             pkv.paged_attention_decode(out, self.q, dk, self.dv, self.dt, self.dl, self.bs,
                                        self.scale, self.dks, self.dvs, partition_size=partition)
         torch.cuda.synchronize()
-        return out.view(torch.int16).cpu().numpy().view(np.uint16)
+        return _unsigned_zero(out.view(torch.int16).cpu().numpy().view(np.uint16))
 
     def expected_row(self, hot):
         """Output bits of one (sequence, kv head) row whose hot tokens are the
@@ -155,7 +162,7 @@ class Probe:
         times their V scales, summed in fp32, then rounded to the output."""
         rows = [self.vvals[b, o, h] * float(self.vs[b, h]) for b, o, h in hot]
         total = np.float32(np.sum(rows, axis=0)) if len(rows) > 1 else np.float32(rows[0])
-        return _out_bits(total / np.float32(len(rows)), self.q_fmt)
+        return _unsigned_zero(_out_bits(total / np.float32(len(rows)), self.q_fmt))
 
 
 def _one_hot_sweep(pkv, p, partition=0, positions=None):
@@ -173,7 +180,7 @@ def _one_hot_sweep(pkv, p, partition=0, positions=None):
         hh = np.broadcast_to(h, (B, hkv))
         kc = p.kbase.copy()
         kc[b, o, hh, 0] = TOP[p.kv_fmt]
-        want = _out_bits(p.vvals[b, o, hh] * p.vs[b, hh][..., None], p.q_fmt)   # [B, Hkv, D]
+        want = _unsigned_zero(_out_bits(p.vvals[b, o, hh] * p.vs[b, hh][..., None], p.q_fmt))
         got = p.run(pkv, kc, partition).reshape(B, hkv, G, p.D)
         bad = np.argwhere((got != want[:, :, None, :]).any(axis=3))
         assert len(bad) == 0, (
@@ -233,9 +240,12 @@ def _two_hot(pkv, p, calls=6, seed=0, partition=0, pick=None):
 
 
 def _lens(seed, n, top, bs):
+    """n lengths in [1, top]: the longest, 1, one block and one block plus a
+    token first, then random ones."""
     rng = np.random.default_rng(seed)
     lens = rng.integers(1, top + 1, n)
-    lens[:3] = [1, bs, bs + 1][: min(3, n)]
+    head = [top, 1, bs, bs + 1]
+    lens[:min(4, n)] = head[:min(4, n)]
     return lens
 
 
@@ -332,11 +342,14 @@ def test_one_byte_shared_prefix_bit_exact(gpu_lib, kv_fmt, q_fmt, group, bs):
     _one_hot_sweep(gpu_lib, p, positions=after_prompt)
 
     def pick(s, h, rng):
-        # one token in the prompt (shared: the same position and code for
-        # every member) and one in the member's own tokens
+        # one token in the prompt (shared: the same position and code 2^6
+        # for every member, so its score is at least 22.6 * 2^(6 - 3) = 181
+        # and every other weight underflows to 0) and one in the member's own
+        # tokens (members whose own block's K scale is the smaller one are
+        # left out: their code would have to exceed 2^6)
         n = int(p.lens[s])
         if member[s]:
-            return (5 + 16 * h) % P, P + int(rng.integers(0, n - P)), 3
+            return (5 + 16 * h) % P, P + int(rng.integers(0, n - P)), 6
         while True:
             t1, t2 = rng.choice(n, 2, replace=False)
             if t1 // p.bs != t2 // p.bs:
