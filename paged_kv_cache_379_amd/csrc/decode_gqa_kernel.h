@@ -25,9 +25,9 @@
 //     MFMA operand layout, 16 rows x 64 bytes per instruction, streams from HBM
 //     at a much lower rate).  The rows are staged in a per-wave LDS tile in
 //     the query's 16-bit format (int8 codes are converted exactly on the way,
-//     [P2] INT8 KV cache), with the row pitch padded by 16 bytes so that both
-//     the row-wise reads of K and the column-wise reads of V hit distinct
-//     banks.  The next block's loads are in flight while the current block is
+//     [P2] INT8 KV cache), with the row pitches padded (16 bytes for K, 32
+//     for V) so that both the row-wise reads of K and the column-wise reads
+//     of V hit distinct banks.  The next block's loads are in flight while the current block is
 //     computed.
 //   * K: lane (t, g) reads 16 bytes of row t, the A operand of S for a
 //     32-element slice of D; Q^T is the B operand, loaded once with the same
@@ -168,8 +168,15 @@ struct GqaTile {
   static constexpr int kSrcRow = D * kEB;             // one token row of one kv head in HBM
   static constexpr int kSrcLanesPerRow = kSrcRow / 16;
   static constexpr int kLoads = kSrcRow / 64;         // 16-byte loads per lane per K (or V) block
-  static constexpr int kPitch = 2 * D + 16;           // LDS row pitch (16-bit elements + pad)
-  static constexpr int kTile = kTileRows * kPitch;    // one tile of K (or V) in LDS
+  // LDS row pitches (16-bit elements + pad).  K rows are read 16 bytes per
+  // lane down a column of rows, so a 16-byte pad puts 16 consecutive rows in
+  // distinct banks; V rows are read 8 bytes per lane across 4 columns of
+  // 8 consecutive rows (the transposing read), so a 32-byte pad does.
+  static constexpr int kPitchK = 2 * D + 16;
+  static constexpr int kPitchV = 2 * D + 32;
+  static constexpr int kTileK = kTileRows * kPitchK;  // one tile of K in LDS
+  static constexpr int kTileV = kTileRows * kPitchV;  // one tile of V, after the K tile
+  static constexpr int kSlot = kTileK + kTileV;       // a staged tile: K, then V
   static constexpr int kSlices = D / 32;              // QK^T MFMAs (32 dims each)
   static constexpr int kTiles = D / 16;               // PV MFMAs (16 dims each)
   static_assert(scaled_format(KF) || KF == QF, "16-bit caches are read in the query's format");
@@ -206,10 +213,12 @@ __device__ __forceinline__ void gqa_load(GqaStage<KF, QF, D>& r, const uint8_t* 
 }
 
 // Staged registers -> the wave's LDS tiles (K, then V) in 16-bit form.
-// soff[c]: LDS byte offset of the 16-bit elements of this lane's load c.
+// soff[c] / voff[c]: LDS byte offset of the 16-bit elements of this lane's
+// load c in the K tile / from the start of the V tile.
 template <int KF, int QF, int D>
 __device__ __forceinline__ void gqa_stage(uint8_t* tile, const GqaStage<KF, QF, D>& r,
-                                          const uint32_t (&soff)[GqaTile<KF, QF, D>::kLoads]) {
+                                          const uint32_t (&soff)[GqaTile<KF, QF, D>::kLoads],
+                                          const uint32_t (&voff)[GqaTile<KF, QF, D>::kLoads]) {
   using T = GqaTile<KF, QF, D>;
 #pragma unroll
   for (int c = 0; c < T::kLoads; ++c) {
@@ -220,11 +229,11 @@ __device__ __forceinline__ void gqa_stage(uint8_t* tile, const GqaStage<KF, QF, 
       const u32x2_t v2 = codes4_to_16<KF, QF>(r.v[c].z), v3 = codes4_to_16<KF, QF>(r.v[c].w);
       *reinterpret_cast<u32x4_t*>(tile + soff[c]) = u32x4_t{k0.x, k0.y, k1.x, k1.y};
       *reinterpret_cast<u32x4_t*>(tile + soff[c] + 16) = u32x4_t{k2.x, k2.y, k3.x, k3.y};
-      *reinterpret_cast<u32x4_t*>(tile + T::kTile + soff[c]) = u32x4_t{v0.x, v0.y, v1.x, v1.y};
-      *reinterpret_cast<u32x4_t*>(tile + T::kTile + soff[c] + 16) = u32x4_t{v2.x, v2.y, v3.x, v3.y};
+      *reinterpret_cast<u32x4_t*>(tile + T::kTileK + voff[c]) = u32x4_t{v0.x, v0.y, v1.x, v1.y};
+      *reinterpret_cast<u32x4_t*>(tile + T::kTileK + voff[c] + 16) = u32x4_t{v2.x, v2.y, v3.x, v3.y};
     } else {
       *reinterpret_cast<u32x4_t*>(tile + soff[c]) = r.k[c];
-      *reinterpret_cast<u32x4_t*>(tile + T::kTile + soff[c]) = r.v[c];
+      *reinterpret_cast<u32x4_t*>(tile + T::kTileK + voff[c]) = r.v[c];
     }
   }
 }
@@ -254,7 +263,7 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
     if (t >= valid || t < lo) {
 #pragma unroll
       for (int c = 0; c < T::kSlices; ++c)
-        *reinterpret_cast<u32x4_t*>(tile + T::kTile + t * T::kPitch + 64 * c + 16 * g) =
+        *reinterpret_cast<u32x4_t*>(tile + T::kTileK + t * T::kPitchV + 64 * c + 16 * g) =
             u32x4_t{0u, 0u, 0u, 0u};
     }
   }
@@ -269,7 +278,7 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
   u32x2_t vt[T::kTiles];
   {
     typedef short i16x4_lds_t __attribute__((ext_vector_type(4)));
-    const uint8_t* vp = tile + T::kTile + (4 * g + t / 4) * T::kPitch + 8 * (t % 4);
+    const uint8_t* vp = tile + T::kTileK + (4 * g + t / 4) * T::kPitchV + 8 * (t % 4);
 #pragma unroll
     for (int c = 0; c < T::kTiles; ++c) {
       const i16x4_lds_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -279,7 +288,7 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
   }
 
   // S = K_blk . Q^T: lane (t, g) reads row t, dims 32c + 8g .. + 7.
-  const uint8_t* krow = tile + t * T::kPitch + 16 * g;
+  const uint8_t* krow = tile + t * T::kPitchK + 16 * g;
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < T::kSlices; ++c)
@@ -347,12 +356,126 @@ __device__ __forceinline__ void gqa_compute(GqaState<KF, QF, D>& st, uint8_t* ti
   }
 }
 
+// Two staged tiles A and B (32 consecutive tokens) in one step: the same
+// arithmetic as gqa_compute on each, with one softmax update for both (one
+// maximum, one rescale decision and one sum over their 32 tokens) and the two
+// score products issued together, so the step's dependent chains overlap.
+// Sixteen distinct query rows (no SPLIT); lo/valid/scales per tile as in
+// gqa_compute.
+template <int KF, int QF, int D>
+__device__ __forceinline__ void gqa_compute_pair(GqaState<KF, QF, D>& st, uint8_t* tileA,
+                                                 uint8_t* tileB,
+                                                 const u32x4_t (&qop)[GqaTile<KF, QF, D>::kSlices],
+                                                 int loA, int validA, int loB, int validB,
+                                                 float kscA, float vscA, float kscB, float vscB,
+                                                 int t, int g, float scale_log2) {
+  using T = GqaTile<KF, QF, D>;
+  using M = Mfma<QF>;
+  typedef short i16x4_lds_t __attribute__((ext_vector_type(4)));
+  // masked rows' V elements to zero (see gqa_compute)
+  auto zero_masked = [&](uint8_t* tile, int lo, int valid) {
+    if (valid < kTileRows || lo > 0) {
+      if (t >= valid || t < lo) {
+#pragma unroll
+        for (int c = 0; c < T::kSlices; ++c)
+          *reinterpret_cast<u32x4_t*>(tile + T::kTileK + t * T::kPitchV + 64 * c + 16 * g) =
+              u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  zero_masked(tileA, loA, validA);
+  zero_masked(tileB, loB, validB);
+  auto read_vt = [&](const uint8_t* tile, u32x2_t (&vt)[T::kTiles]) {
+    const uint8_t* vp = tile + T::kTileK + (4 * g + t / 4) * T::kPitchV + 8 * (t % 4);
+#pragma unroll
+    for (int c = 0; c < T::kTiles; ++c)
+      vt[c] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                              (__attribute__((address_space(3))) i16x4_lds_t*)(vp + 32 * c)));
+  };
+  u32x2_t vt[T::kTiles];
+  read_vt(tileA, vt);
+
+  // both score products, interleaved
+  const uint8_t* krowA = tileA + t * T::kPitchK + 16 * g;
+  const uint8_t* krowB = tileB + t * T::kPitchK + 16 * g;
+  f32x4_t sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < T::kSlices; ++c) {
+    sA = M::k32(*reinterpret_cast<const u32x4_t*>(krowA + 64 * c), qop[c], sA);
+    sB = M::k32(*reinterpret_cast<const u32x4_t*>(krowB + 64 * c), qop[c], sB);
+  }
+
+  const float scA = scale_log2 * kscA, scB = scale_log2 * kscB;
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sv[i] = (4 * g + i < validA && 4 * g + i >= loA) ? sA[i] * scA : -INFINITY;
+    sv[4 + i] = (4 * g + i < validB && 4 * g + i >= loB) ? sB[i] * scB : -INFINITY;
+  }
+  float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                   fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false, false);
+    bm = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  }
+  const bool raise = bm > st.m + kRescaleSlack;
+  if (__ballot(raise) != 0) {
+    const float mn = raise ? bm : st.m;
+    const float alpha = fast_exp2(st.m - mn);
+    st.l *= alpha;
+    if (__ballot(raise && st.m != -INFINITY) != 0) {
+#pragma unroll
+      for (int c = 0; c < T::kTiles; ++c) st.acc[c] *= alpha;
+    }
+    st.m = mn;
+  }
+  const float ms = (st.m == -INFINITY) ? 0.f : st.m;
+  float w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = fast_exp2(sv[i] - ms);
+  {
+    float ps = ((w[0] + w[1]) + (w[2] + w[3])) + ((w[4] + w[5]) + (w[6] + w[7]));
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+    ps = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(ps), __float_as_uint(ps), false, false);
+    st.l += __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[i] *= vscA;
+    w[4 + i] *= vscB;
+  }
+  // P^T operands of each tile as hi + lo parts
+  auto pack = [&](const float* x, u32x2_t& hi, u32x2_t& lo) {
+    const uint32_t h01 = M::pack(x[0], x[1]), h23 = M::pack(x[2], x[3]);
+    hi = u32x2_t{h01, h23};
+    lo = u32x2_t{M::pack(x[0] - M::lo_value(h01), x[1] - M::hi_value(h01)),
+                 M::pack(x[2] - M::lo_value(h23), x[3] - M::hi_value(h23))};
+  };
+  u32x2_t pA_hi, pA_lo, pB_hi, pB_lo;
+  pack(w, pA_hi, pA_lo);
+  pack(w + 4, pB_hi, pB_lo);
+#pragma unroll
+  for (int c = 0; c < T::kTiles; ++c) {
+    st.acc[c] = M::k16(vt[c], pA_hi, st.acc[c]);
+    st.acc[c] = M::k16(vt[c], pA_lo, st.acc[c]);
+  }
+  read_vt(tileB, vt);
+#pragma unroll
+  for (int c = 0; c < T::kTiles; ++c) {
+    st.acc[c] = M::k16(vt[c], pB_hi, st.acc[c]);
+    st.acc[c] = M::k16(vt[c], pB_lo, st.acc[c]);
+  }
+}
+
 // LDS of one grouped-query workgroup: per-wave K/V tiles during the loop,
 // whose bytes then hold the waves' accumulators for the final merge, and the
 // waves' softmax states.
 template <int KF, int QF, int D, int NW>
 struct GqaShared {
-  static constexpr int kStageBytes = NW * 2 * GqaTile<KF, QF, D>::kTile;
+  static constexpr int kStageBytes = NW * GqaTile<KF, QF, D>::kSlot;
   static constexpr int kAccRow = D + 4;  // padded: the 16 columns' rows start in different banks
   static constexpr int kMergeBytes = NW * 16 * kAccRow * 4;
   static constexpr int kTileBytes = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
@@ -454,12 +577,12 @@ __device__ __forceinline__ void gqa_decode_body(const DecodeArgs& a, int item, u
   const int64_t head_off = static_cast<int64_t>(kvh) * T::kSrcRow;
   const uint8_t* kbase = a.key_cache + head_off;
   const uint8_t* vbase = a.value_cache + head_off;
-  uint8_t* tile = smem + wave * 2 * T::kTile;
+  uint8_t* tile = smem + wave * T::kSlot;
   // Per load c: global byte offset of this lane's 16 source bytes from the
   // first row of its block's part of the tile, whether that is the tile's
   // second block (two blocks per tile), and the LDS offset of their 16-bit
   // form.
-  uint32_t goff[T::kLoads], soff[T::kLoads];
+  uint32_t goff[T::kLoads], soff[T::kLoads], voff[T::kLoads];
   bool second[T::kLoads];
 #pragma unroll
   for (int c = 0; c < T::kLoads; ++c) {
@@ -468,7 +591,8 @@ __device__ __forceinline__ void gqa_decode_body(const DecodeArgs& a, int item, u
     const int ch = idx % T::kSrcLanesPerRow;
     second[c] = kTwo && r >= BS;
     goff[c] = static_cast<uint32_t>((kTwo ? r % BS : r) * row_stride + 16 * ch);
-    soff[c] = static_cast<uint32_t>(r * T::kPitch + 16 * ch * (2 / T::kEB));
+    soff[c] = static_cast<uint32_t>(r * T::kPitchK + 16 * ch * (2 / T::kEB));
+    voff[c] = static_cast<uint32_t>(r * T::kPitchV + 16 * ch * (2 / T::kEB));
   }
 
   // Tiles of this wave: pt0 + wave + NW * k for k < nk.  The loads of tile
@@ -551,14 +675,14 @@ __device__ __forceinline__ void gqa_decode_body(const DecodeArgs& a, int item, u
         gqa_load<KF, QF, D, kTwo>(r1, kbase, vbase, oa, ob, goff, second);
       }
       for (int k = 0; k < kend; k += 2) {
-        gqa_stage(tile, r0, soff);
+        gqa_stage(tile, r0, soff, voff);
         if (k + 2 < kend) {
           offsets(k + 2, oa, ob);
           gqa_load<KF, QF, D, kTwo>(r0, kbase, vbase, oa, ob, goff, second);
         }
         compute(k);
         if (k + 1 < kend) {
-          gqa_stage(tile, r1, soff);
+          gqa_stage(tile, r1, soff, voff);
           if (k + 3 < kend) {
             offsets(k + 3, oa, ob);
             gqa_load<KF, QF, D, kTwo>(r1, kbase, vbase, oa, ob, goff, second);
@@ -568,7 +692,7 @@ __device__ __forceinline__ void gqa_decode_body(const DecodeArgs& a, int item, u
       }
     } else {
       for (int k = 0; k < kend; ++k) {
-        gqa_stage(tile, r0, soff);
+        gqa_stage(tile, r0, soff, voff);
         if (k + 1 < kend) {
           offsets(k + 1, oa, ob);
           gqa_load<KF, QF, D, kTwo>(r0, kbase, vbase, oa, ob, goff, second);

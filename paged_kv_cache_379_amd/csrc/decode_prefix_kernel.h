@@ -31,10 +31,10 @@ struct PrefixArgs {
   int work_start[kMaxPrefixGroups + 1];   // first workgroup of each group
 };
 
-// LDS of one prefix workgroup: two buffers of a K tile and a V tile.
+// LDS of one prefix workgroup: two buffers of two K tiles and two V tiles.
 template <int KF, int QF, int D>
 struct PrefixShared {
-  static constexpr int kBytes = 2 * 2 * GqaTile<KF, QF, D>::kTile;
+  static constexpr int kBytes = 2 * 2 * GqaTile<KF, QF, D>::kSlot;
 };
 
 // Prefix work item `item` (group, kv head, row tile, chunk), with `smem` the
@@ -128,7 +128,8 @@ __device__ __forceinline__ void prefix_body(const PrefixArgs& pa, int item, uint
   const bool loads = lane < kLoadLanes;
   const int trow_in = 4 * wave + (loads ? lane / T::kSrcLanesPerRow : 0);
   const int tch = loads ? lane % T::kSrcLanesPerRow : 0;
-  const uint32_t soff = static_cast<uint32_t>(trow_in * T::kPitch + 16 * tch * (2 / T::kEB));
+  const uint32_t soff = static_cast<uint32_t>(trow_in * T::kPitchK + 16 * tch * (2 / T::kEB));
+  const uint32_t voff = static_cast<uint32_t>(T::kTileK + trow_in * T::kPitchV + 16 * tch * (2 / T::kEB));
   auto src_offset = [&](int k) -> int64_t {
     const int jj = c0 / kTileRows + k;
     if constexpr (kTwo) {
@@ -144,10 +145,7 @@ __device__ __forceinline__ void prefix_body(const PrefixArgs& pa, int item, uint
              16 * tch;
     }
   };
-  // One tile's 16 source bytes of K and of V per loading lane.  Two sets
-  // alternate so that tiles k + 1 and k + 2 are in flight while tile k is
-  // computed (a third set measured no faster and cost the kernel a wave per
-  // SIMD: 203 registers against 157).
+  // One tile's 16 source bytes of K and of V per loading lane.
   struct TileRegs {
     u32x4_t k, v;
   };
@@ -167,11 +165,11 @@ __device__ __forceinline__ void prefix_body(const PrefixArgs& pa, int item, uint
         const u32x2_t v2 = codes4_to_16<KF, QF>(r.v.z), v3 = codes4_to_16<KF, QF>(r.v.w);
         *reinterpret_cast<u32x4_t*>(tile + soff) = u32x4_t{k0.x, k0.y, k1.x, k1.y};
         *reinterpret_cast<u32x4_t*>(tile + soff + 16) = u32x4_t{k2.x, k2.y, k3.x, k3.y};
-        *reinterpret_cast<u32x4_t*>(tile + T::kTile + soff) = u32x4_t{v0.x, v0.y, v1.x, v1.y};
-        *reinterpret_cast<u32x4_t*>(tile + T::kTile + soff + 16) = u32x4_t{v2.x, v2.y, v3.x, v3.y};
+        *reinterpret_cast<u32x4_t*>(tile + voff) = u32x4_t{v0.x, v0.y, v1.x, v1.y};
+        *reinterpret_cast<u32x4_t*>(tile + voff + 16) = u32x4_t{v2.x, v2.y, v3.x, v3.y};
       } else {
         *reinterpret_cast<u32x4_t*>(tile + soff) = r.k;
-        *reinterpret_cast<u32x4_t*>(tile + T::kTile + soff) = r.v;
+        *reinterpret_cast<u32x4_t*>(tile + voff) = r.v;
       }
     }
   };
@@ -182,12 +180,20 @@ __device__ __forceinline__ void prefix_body(const PrefixArgs& pa, int item, uint
 #pragma unroll
   for (int c = 0; c < T::kTiles; ++c) st.acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int k) {
-    uint8_t* tile = smem + (k & 1) * 2 * T::kTile;
+  // Attended rows lo <= row < valid of tile k and its scales (as in the
+  // grouped-query kernel); a tile past the chunk's end attends nothing.
+  auto tile_params = [&](int k, int& lo, int& valid, float& ks, float& vs) {
+    lo = 0;
+    valid = kTileRows;
+    ks = 1.f;
+    vs = 1.f;
+    if (k >= ntiles) {
+      valid = 0;
+      return;
+    }
     const int p = __builtin_amdgcn_readlane(tb, k);
-    int lo = 0, valid = kTileRows;
-    float ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k));
-    float vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k));
+    ks = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tks), k));
+    vs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tvs), k));
     if constexpr (kTwo) {
       const int p2 = __builtin_amdgcn_readlane(tb2, k);
       if (p < 0) lo = BS;
@@ -199,28 +205,42 @@ __device__ __forceinline__ void prefix_body(const PrefixArgs& pa, int item, uint
     } else {
       if (p < 0) valid = 0;
     }
-    gqa_compute<KF, QF, D, false>(st, tile, qop, lo, valid, ks, vs, t, g, a.scale_log2);
   };
-  // Tile k: compute it from LDS, stage tile k + 1 (in `next`), reload `next`
-  // with tile k + 3.  Two sets: tiles k + 1 and k + 2 in flight.
-  auto step = [&](int k, TileRegs& next) {
-    compute(k);
-    if (k + 1 < ntiles) stage_tile(smem + ((k + 1) & 1) * 2 * T::kTile, next);
-    load_tile(next, k + 3);
-    __syncthreads();
+  // The tiles go in pairs (2j, 2j + 1), one softmax update per pair; an odd
+  // count ends with a pair whose second tile attends nothing.  LDS holds two
+  // pairs: pair j is computed from buffer j & 1 while pair j + 1 is staged in
+  // the other one and pair j + 2 loads into registers (two tiles in flight).
+  constexpr int kPairBytes = 2 * T::kSlot;
+  auto compute_pair = [&](int j) {
+    uint8_t* pair = smem + (j & 1) * kPairBytes;
+    int loA, validA, loB, validB;
+    float ksA, vsA, ksB, vsB;
+    tile_params(2 * j, loA, validA, ksA, vsA);
+    tile_params(2 * j + 1, loB, validB, ksB, vsB);
+    gqa_compute_pair<KF, QF, D>(st, pair, pair + T::kSlot, qop, loA, validA, loB, validB, ksA,
+                                vsA, ksB, vsB, t, g, a.scale_log2);
+  };
+  auto stage_pair = [&](int j, const TileRegs& ra, const TileRegs& rb) {
+    uint8_t* pair = smem + (j & 1) * kPairBytes;
+    stage_tile(pair, ra);
+    stage_tile(pair + T::kSlot, rb);
   };
 
   if (ntiles > 0) {
-    TileRegs r0, r1;
-    load_tile(r0, 0);
-    load_tile(r1, 1);
-    stage_tile(smem, r0);
-    load_tile(r0, 2);
+    const int npairs = (ntiles + 1) / 2;
+    TileRegs ra, rb;
+    load_tile(ra, 0);
+    load_tile(rb, 1);
+    stage_pair(0, ra, rb);
+    load_tile(ra, 2);
+    load_tile(rb, 3);
     __syncthreads();
-    for (int k = 0; k < ntiles; k += 2) {
-      step(k, r1);
-      if (k + 1 >= ntiles) break;
-      step(k + 1, r0);
+    for (int j = 0; j < npairs; ++j) {
+      compute_pair(j);
+      if (j + 1 < npairs) stage_pair(j + 1, ra, rb);
+      load_tile(ra, 2 * j + 4);
+      load_tile(rb, 2 * j + 5);
+      __syncthreads();
     }
   }
 
@@ -254,7 +274,7 @@ __global__ void __launch_bounds__(kPrefixWaves * 64) paged_prefix_kernel(PrefixA
 // launch.  (Dealing the two kinds in alternating runs measured slower at long
 // prefixes: the rest items then compete with every prefix chunk.)
 template <int KF, int QF, int D, bool SPLIT, int BS>
-__global__ void __launch_bounds__(kPrefixWaves * 64)
+__global__ void __launch_bounds__(kPrefixWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
     paged_prefix_fused_kernel(PrefixArgs pa, int n_prefix) {
   static_assert(kPrefixWaves == 4, "both kinds run on four waves");
   constexpr int kP = PrefixShared<KF, QF, D>::kBytes;
