@@ -392,8 +392,10 @@ __device__ __forceinline__ void gqa_compute_pair(GqaState<KF, QF, D>& st, uint8_
       vt[c] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                               (__attribute__((address_space(3))) i16x4_lds_t*)(vp + 32 * c)));
   };
-  u32x2_t vt[T::kTiles];
+  // both tiles' V^T operands first, their latency hidden by the scores
+  u32x2_t vt[T::kTiles], vtB[T::kTiles];
   read_vt(tileA, vt);
+  read_vt(tileB, vtB);
 
   // both score products, interleaved
   const uint8_t* krowA = tileA + t * T::kPitchK + 16 * g;
@@ -447,26 +449,24 @@ __device__ __forceinline__ void gqa_compute_pair(GqaState<KF, QF, D>& st, uint8_
     w[i] *= vscA;
     w[4 + i] *= vscB;
   }
-  // P^T operands of each tile as hi + lo parts
-  auto pack = [&](const float* x, u32x2_t& hi, u32x2_t& lo) {
-    const uint32_t h01 = M::pack(x[0], x[1]), h23 = M::pack(x[2], x[3]);
-    hi = u32x2_t{h01, h23};
-    lo = u32x2_t{M::pack(x[0] - M::lo_value(h01), x[1] - M::hi_value(h01)),
-                 M::pack(x[2] - M::lo_value(h23), x[3] - M::hi_value(h23))};
-  };
-  u32x2_t pA_hi, pA_lo, pB_hi, pB_lo;
-  pack(w, pA_hi, pA_lo);
-  pack(w + 4, pB_hi, pB_lo);
+  // O^T += V^T . P^T over the pair's 32 tokens in one 16x16x32 product per
+  // 16 dims (and per hi/lo part).  The contraction index k = 8g + j of lane
+  // (t, g) stands for token 4g + j of tile A (j < 4) and token 4g + j - 4 of
+  // tile B (j >= 4): exactly the V^T elements of the two transposing reads
+  // and the weights this lane computed, side by side; the sum over k does not
+  // depend on how tokens map to it.
+  const uint32_t a01 = M::pack(w[0], w[1]), a23 = M::pack(w[2], w[3]);
+  const uint32_t b01 = M::pack(w[4], w[5]), b23 = M::pack(w[6], w[7]);
+  const u32x4_t p_hi = {a01, a23, b01, b23};
+  const u32x4_t p_lo = {M::pack(w[0] - M::lo_value(a01), w[1] - M::hi_value(a01)),
+                        M::pack(w[2] - M::lo_value(a23), w[3] - M::hi_value(a23)),
+                        M::pack(w[4] - M::lo_value(b01), w[5] - M::hi_value(b01)),
+                        M::pack(w[6] - M::lo_value(b23), w[7] - M::hi_value(b23))};
 #pragma unroll
   for (int c = 0; c < T::kTiles; ++c) {
-    st.acc[c] = M::k16(vt[c], pA_hi, st.acc[c]);
-    st.acc[c] = M::k16(vt[c], pA_lo, st.acc[c]);
-  }
-  read_vt(tileB, vt);
-#pragma unroll
-  for (int c = 0; c < T::kTiles; ++c) {
-    st.acc[c] = M::k16(vt[c], pB_hi, st.acc[c]);
-    st.acc[c] = M::k16(vt[c], pB_lo, st.acc[c]);
+    const u32x4_t va = {vt[c].x, vt[c].y, vtB[c].x, vtB[c].y};
+    st.acc[c] = M::k32(va, p_hi, st.acc[c]);
+    st.acc[c] = M::k32(va, p_lo, st.acc[c]);
   }
 }
 
