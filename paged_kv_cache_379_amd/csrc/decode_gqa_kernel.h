@@ -411,8 +411,15 @@ __device__ __forceinline__ void gqa_compute_pair(GqaState<KF, QF, D>& st, uint8_
   float sv[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    sv[i] = (4 * g + i < validA && 4 * g + i >= loA) ? sA[i] * scA : -INFINITY;
-    sv[4 + i] = (4 * g + i < validB && 4 * g + i >= loB) ? sB[i] * scB : -INFINITY;
+    sv[i] = sA[i] * scA;
+    sv[4 + i] = sB[i] * scB;
+  }
+  if (loA > 0 || validA < kTileRows || loB > 0 || validB < kTileRows) {  // wave-uniform
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * g + i >= validA || 4 * g + i < loA) sv[i] = -INFINITY;
+      if (4 * g + i >= validB || 4 * g + i < loB) sv[4 + i] = -INFINITY;
+    }
   }
   float bm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                    fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
