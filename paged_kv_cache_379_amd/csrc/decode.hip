@@ -34,11 +34,20 @@ namespace {
 // kSplitTokens tokens, so a few long sequences among short ones do not leave a
 // tail of long-running workgroups.  Independently, the grid is split further
 // until it has at least kMinItems workgroups (two per CU), so small batches
-// still fill the chip.  Partitions are whole multiples of
-// partition_align(block_size) tokens.
+// still fill the chip, but not into partitions shorter than span / 32
+// (clamped to kMinPartTokens .. kMaxFloorTokens): each partition adds a
+// partial to write and merge and the merge is a second launch, so a few
+// (sequence, kv head) pairs do best with a few dozen partitions of at least
+// 128 tokens, and a table of at most 128 tokens stays whole.  Measured on
+// MI355X with 8 pairs (HIP events, cold caches; automatic before this floor
+// -> with it): 112 tokens 12.4 -> 8.2 us, 1024 tokens 17.2 -> 12.7, 2048
+// 17.5 -> 13.5, 4096 18.6 -> 16.0, 16384 27.0 -> 23.4, 32768 37.3 -> 33.3.
+// Partitions are whole multiples of partition_align(block_size) tokens.
 constexpr int64_t kWholeTokens = 2560;
 constexpr int64_t kSplitTokens = 1024;
 constexpr int64_t kMinItems = 512;
+constexpr int64_t kMinPartTokens = 128;
+constexpr int64_t kMaxFloorTokens = 1024;
 // With a sliding window every context longer than the window attends exactly
 // the window, so whole windows give equal workgroups and no tail to split
 // away; the grid is then split only below one workgroup per CU.  Measured on
@@ -102,7 +111,9 @@ int64_t partition_tokens(int num_seqs, int num_kv_heads, int64_t span, int block
   const int64_t pairs = static_cast<int64_t>(num_seqs) * num_kv_heads;
   if (pairs > 0 && pairs * ((span + pt - 1) / pt) < min_items) {
     const int64_t parts = (min_items + pairs - 1) / pairs;
-    pt = ((span + parts - 1) / parts + u - 1) / u * u;
+    const int64_t floor_tokens = std::min(std::max(span / 32, kMinPartTokens), kMaxFloorTokens);
+    pt = std::max((span + parts - 1) / parts, floor_tokens);
+    pt = (pt + u - 1) / u * u;
   }
   return pt < u ? u : (pt > span ? span : pt);
 }

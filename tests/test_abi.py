@@ -79,10 +79,15 @@ def test_workspace_size_and_partition_policy():
     # ... longer tables split into 1024-token partitions
     assert pkv.decode_partition_size(256, 32, 8, 128, 16, 256) == 1024   # int8 config, 4096 max
     assert pkv.decode_workspace_size(256, 32, 8, 128, 16, 256) == 256 * 32 * 4 * 130 * 4
-    # ... and small grids split further, to at least 512 workgroups
-    assert pkv.decode_partition_size(1, 8, 8, 128, 16, 2048) == 512      # 1 seq, 32k tokens
-    assert pkv.decode_partition_size(2, 4, 4, 64, 16, 7) == 16           # tiny: 7 partitions
-    assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7) == 2 * 4 * 7 * 66 * 4
+    # ... and small grids split further, towards 512 workgroups, but not into
+    # partitions shorter than span / 32 (clamped to 128 .. 1024 tokens)
+    assert pkv.decode_partition_size(1, 8, 8, 128, 16, 2048) == 1024     # 1 seq, 32k tokens: 32 parts
+    assert pkv.decode_partition_size(1, 8, 8, 128, 16, 256) == 128       # 4096 tokens: 32 parts
+    assert pkv.decode_partition_size(4, 32, 8, 128, 16, 64) == 128      # 1024 tokens: 8 parts
+    assert pkv.decode_partition_size(2, 4, 4, 64, 16, 7) == 0            # tiny (112 tokens): whole
+    assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 7) == 0
+    assert pkv.decode_partition_size(2, 4, 4, 64, 16, 9) == 128          # 144 tokens: 2 parts
+    assert pkv.decode_workspace_size(2, 4, 4, 64, 16, 9) == 2 * 4 * 2 * 66 * 4
     # explicit sizes; one as long as the table means no split and no workspace
     assert pkv.decode_partition_size(32, 64, 64, 128, 16, 128, 512) == 512
     assert pkv.decode_workspace_size(32, 64, 64, 128, 16, 128, 512) == 32 * 64 * 4 * 130 * 4
@@ -120,11 +125,14 @@ def test_partition_policy_other_block_sizes():
         assert pkv.decode_partition_size(32, 64, 64, 128, bs, mb) == 0           # 2048 tokens whole
         assert pkv.decode_partition_size(256, 32, 8, 128, bs, 4096 // bs) == 1024
         assert pkv.decode_workspace_size(256, 32, 8, 128, bs, 4096 // bs) == 256 * 32 * 4 * 130 * 4
-        # few sequences: shrink until 512 workgroups (2 seqs x 2 kv heads -> 128 parts)
+        # few sequences: shrink towards 512 workgroups, down to span / 32
+        # (2 seqs x 2 kv heads, 4096 tokens -> 32 parts of 128)
         pt = pkv.decode_partition_size(2, 4, 2, 64, bs, 4096 // bs)
-        assert pt == 32 and pt % max(bs, 16) == 0
-    assert pkv.decode_partition_size(2, 4, 2, 64, 8, 7) == 16   # 56 tokens -> span 64, 4 parts of 16
-    assert pkv.decode_workspace_size(2, 4, 2, 64, 8, 7) == 2 * 4 * 4 * 66 * 4
+        assert pt == 128 and pt % max(bs, 16) == 0
+    assert pkv.decode_partition_size(2, 4, 2, 64, 8, 7) == 0    # 56 tokens: whole
+    assert pkv.decode_workspace_size(2, 4, 2, 64, 8, 7) == 0
+    assert pkv.decode_partition_size(2, 4, 2, 64, 8, 20) == 128  # 160 tokens: 2 parts
+    assert pkv.decode_workspace_size(2, 4, 2, 64, 8, 20) == 2 * 4 * 2 * 66 * 4
     assert pkv.decode_partition_size(2, 4, 4, 64, 8, 8, 8) == 0  # 8 tokens: not a multiple of 16
     assert pkv.decode_partition_size(2, 4, 4, 64, 32, 8, 16) == 0
     assert pkv.decode_partition_size(2, 4, 4, 64, 32, 8, 64) == 64

@@ -128,10 +128,10 @@ def test_random_cache_write_bit_exact(gpu_lib, k):
 
 @pytest.mark.parametrize("k", range(24))
 def test_random_long_context_parity(gpu_lib, k):
-    """Long contexts (up to 12000 tokens) on small grids, automatic
-    partitioning: a few (sequence, kv head) pairs split into hundreds of
-    partitions (the merge then takes several passes of its lanes), optional
-    long sliding windows."""
+    """Long contexts (up to 12000 tokens) on small grids: a few (sequence, kv
+    head) pairs split into dozens of partitions by the automatic policy (even
+    k), or into about a hundred 96-token partitions (odd k: the merge then
+    takes several passes of its lanes); optional long sliding windows."""
     from test_gpu_decode import _behind_window
     rng = np.random.default_rng(13000 + k)
     kv_fmt, q_fmt = FORMATS[rng.integers(len(FORMATS))]
@@ -147,10 +147,12 @@ def test_random_long_context_parity(gpu_lib, k):
                          max_blocks=-(-12000 // bs) + 1, block_size=bs, poison_unused=True)
     if window:
         wl = _behind_window(wl, window)
+    partition = 96 if k % 2 else 0          # a multiple of every block size's alignment
     ref = oracle_decode(wl, window=window)
-    got = out_f64(gpu_decode(gpu_lib, wl, window=window))
+    got = out_f64(gpu_decode(gpu_lib, wl, partition_size=partition, window=window))
     assert_parity(got, ref, kv_fmt, q_fmt, with_output_rounding=True,
-                  label=f"{kv_fmt}/{q_fmt} bs={bs} G={group} Hkv={kv_heads} lens={lens} W={window}")
+                  label=f"{kv_fmt}/{q_fmt} bs={bs} G={group} Hkv={kv_heads} lens={lens} W={window} "
+                        f"partition={partition}")
 
 
 @pytest.mark.parametrize("k", range(20))
