@@ -24,8 +24,8 @@ least 768 MiB of other cache data passes between two uses of one copy), so a
 step reads its K/V from HBM, not from the MALL the previous step filled; the
 event-timed sweeps fill a 512 MiB buffer before each timed call for the same
 reason.  ``read_probe_gbps`` is the library's read-only streaming probe
-(the decode's loads over 2 GiB), the read bandwidth a decode can reach on
-this GPU.  ``cpu_baseline`` times the CPU
+(the decode's loads over 2 GiB, one contiguous stretch per workgroup), the
+read bandwidth of a plain stream on this GPU.  ``cpu_baseline`` times the CPU
 oracle (test infrastructure, fp64 NumPy) on a bounded sample of the same
 workload on this host.
 

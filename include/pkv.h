@@ -350,8 +350,8 @@ int pkv_stream_copy(void* dst, const void* src, size_t bytes, void* stream);
 /*
  * Read-only streaming probe over `bytes` bytes of device memory at `src` (a
  * multiple of 16, 16-byte aligned) with the decode's loads (16-byte,
- * non-temporal): the reference point for the read bandwidth a decode can
- * reach.  Each thread folds the words it read with XOR and writes the fold to
+ * non-temporal), each workgroup reading one contiguous stretch: the reference
+ * point for the read bandwidth of a plain stream.  Each thread folds the words it read with XOR and writes the fold to
  * the device word `sink` only when it equals `sentinel`, so that no load can
  * be optimised away; `sink` must be a writable device word (its content
  * after the call is unspecified unless some fold equals the sentinel).

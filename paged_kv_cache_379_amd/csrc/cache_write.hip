@@ -273,28 +273,33 @@ __global__ void __launch_bounds__(kStreamThreads) stream_copy_kernel(uint4* __re
   for (; i < nvec; i += stride) dst[i] = src[i];
 }
 
-// Read-only streaming probe with the decode's loads (16-byte, non-temporal),
-// eight in flight per thread.  Each thread folds what it read with XOR and
-// stores the fold to the sink only if it equals the sentinel, a run-time
-// value, so no load can be dropped.
-constexpr int kReadUnroll = 8;
+// Read-only streaming probe with the decode's loads (16-byte, non-temporal).
+// Each workgroup reads one contiguous stretch of the buffer, kReadUnroll
+// 4 KiB pieces in flight: measured on MI355X over 2 GiB, 7.0-7.1 TB/s, against
+// 6.2-6.3 TB/s when the whole grid sweeps the buffer together (each
+// workgroup's pieces a grid's width apart).  Each thread folds what it read
+// with XOR and stores the fold to the sink only if it equals the sentinel, a
+// run-time value, so no load can be dropped.
+constexpr int kReadUnroll = 16;
 
 __global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const uint4* __restrict__ src,
                                                                      int64_t nvec, uint32_t* sink,
                                                                      uint32_t sentinel) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kStreamThreads;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * kStreamThreads + threadIdx.x;
+  const int64_t per = (nvec + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int64_t b1 = b0 + per < nvec ? b0 + per : nvec;
+  int64_t i = b0 + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + (kReadUnroll - 1) * stride < nvec; i += kReadUnroll * stride) {
+  for (; i + (kReadUnroll - 1) * kStreamThreads < b1; i += kReadUnroll * kStreamThreads) {
     u32x4 r[kReadUnroll];
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u)
-      r[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i + u * stride));
+      r[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + i + u * kStreamThreads));
 #pragma unroll
     for (int u = 0; u < kReadUnroll; ++u) acc ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
   }
-  for (; i < nvec; i += stride) {
+  for (; i < b1; i += kStreamThreads) {
     const uint4 r = src[i];
     acc ^= r.x ^ r.y ^ r.z ^ r.w;
   }
@@ -471,6 +476,7 @@ int pkv_stream_read(const void* src, size_t bytes, uint32_t* sink, uint32_t sent
   if (!src || !sink || bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16)
     return pkv::fail(PKV_ERR_INVALID_ARG, "NULL or misaligned pointer, or size not a multiple of 16");
   const int64_t nvec = static_cast<int64_t>(bytes / 16);
+  // 8192 workgroups (32 per CU): stretches of 256 KiB over 2 GiB
   int64_t blocks = (nvec + kStreamThreads * kReadUnroll - 1) / (kStreamThreads * kReadUnroll);
   if (blocks > 256 * 32) blocks = 256 * 32;
   hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kStreamThreads),
