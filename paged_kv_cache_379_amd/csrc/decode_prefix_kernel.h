@@ -6,10 +6,11 @@
 // A workgroup takes one kv head of one group, 64 query rows (the group's
 // (sequence, query head) pairs of that kv head, 16 per wave as the 16 MFMA
 // columns) and one chunk of the prefix.  The four waves load each 16-token
-// tile of the prefix together (a quarter each), stage it once in LDS (double
-// buffered, one barrier per tile), and every wave runs the grouped-query
-// kernel's tile step (scores, online softmax, weighted V sum) on it with its
-// own 16 rows.  The partial (max, sum, accumulator) of each row goes to the
+// tile of the prefix together (a quarter each) and stage it once in LDS; the
+// tiles go in pairs (double buffered, one barrier per pair), and every wave
+// runs the grouped-query arithmetic on a pair at a time (scores, one online
+// softmax update for its 32 tokens, weighted V sum) with its own 16 rows.
+// The partial (max, sum, accumulator) of each row goes to the
 // workspace slot of its chunk; the merge kernel combines the chunks with the
 // partials of the rest of each context, which the decode kernels compute (for
 // grouped-query heads in the same launch, after the prefix items).
@@ -50,7 +51,6 @@ __device__ __forceinline__ void prefix_body(const PrefixArgs& pa, int item, uint
   constexpr int kLoadLanes = 4 * T::kSrcLanesPerRow;
   static_assert(kLoadLanes <= 64, "a quarter tile per wave in one load");
   const DecodeArgs& a = pa.d;
-
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
