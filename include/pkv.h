@@ -78,13 +78,15 @@ int pkv_abi_version(void);
  * automatic choice depends on shapes only (never on device data): with
  * span = max_blocks_per_seq * block_size rounded up to U, a span of up to 2560
  * tokens is not split, a longer one is split into 1024-token partitions, and
- * the partitions are made smaller (in steps of U) until
- * num_seqs * num_kv_heads * partitions >= 512.  With a sliding window W that
- * is shorter than the table, the span is W + U - 1 rounded up to U, it is not
- * split by length (every context longer than W attends exactly W tokens),
- * and it is split into equal partitions only until
- * num_seqs * num_kv_heads * partitions >= 256.  The partitions of a sequence
- * start at its first attended token rounded down to U.
+ * the partitions are made smaller towards
+ * num_seqs * num_kv_heads * partitions >= 512, but not below span / 32
+ * tokens clamped to 128 .. 1024 (so a span of at most 128 tokens stays
+ * whole).  With a sliding window W that is shorter than the table, the span
+ * is W + U - 1 rounded up to U, it is not split by length (every context
+ * longer than W attends exactly W tokens), and it is split into equal
+ * partitions only towards num_seqs * num_kv_heads * partitions >= 256, with
+ * the same floor.  Partitions are rounded up to U.  The partitions of a
+ * sequence start at its first attended token rounded down to U.
  */
 int pkv_decode_partition_size(int num_seqs, int num_heads, int num_kv_heads,
                               int head_dim, int block_size,
