@@ -119,8 +119,11 @@ size_t pkv_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads,
  *       kv head, or an fp32 cache), 1 = grouped-query kernel on the matrix
  *       cores,
  *   [4] workgroups of the decode launch.
- * Depends on shapes only, never on device data.  Errors: INVALID_ARG (bad
- * shape, partition size or format), UNSUPPORTED (block size).
+ * Depends on shapes and on the current device's compute-unit count (see the
+ * length-balanced order under pkv_paged_attention_decode; without a device
+ * the plan is the one without that order), never on device data.  Errors:
+ * INVALID_ARG (bad shape, partition size or format), UNSUPPORTED (block
+ * size).
  */
 int pkv_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int block_size,
                     int max_blocks_per_seq, int partition_size, int sliding_window, int kv_dtype,
@@ -176,6 +179,12 @@ int pkv_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
  *   workspace    device scratch of >= pkv_decode_workspace_size(...) bytes
  *                (may be NULL when that is 0); fully rewritten by each call,
  *                so calls that share a workspace must be stream-ordered
+ *
+ * Scheduling (not part of the result): batches of 2..64 sequences decoded
+ * by the multi-head kernel with whole contexts, whose grid fills the GPU's
+ * compute units once to four times, are dealt to the workgroups by context
+ * length (each workgroup reads all lengths), so that every compute unit gets
+ * long and short contexts alike; equal lengths keep the batch order.
  *
  * A block id outside [0, num_blocks) in a position that is read makes that
  * block's tokens count as masked (output unspecified but finite, no

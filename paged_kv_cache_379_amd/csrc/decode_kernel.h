@@ -74,6 +74,10 @@ struct DecodeArgs {
   int num_parts;    // partitions per sequence in the grid
   int window;       // sliding window in tokens, 0 = the whole context
   int heads_per_item;  // multi-head kernel: kv heads per workgroup (1, 2 or 4)
+  // Multi-head kernel: > 0 deals the (at most 64) sequences to the grid's
+  // sequence positions by context length in runs of balance_run ranks
+  // (balanced_seq); 0 keeps the batch order.
+  int balance_run;
   float scale_log2; // scale * log2(e)
   // Shared-prefix decode: the first prefix_lens[s] tokens of sequence s are
   // attended by the prefix kernel, which writes its partials to the first
@@ -88,6 +92,36 @@ struct DecodeArgs {
   // chunks itself and stores the output.
   int merge_prefix;
 };
+
+// The sequence that sequence position `pos` of the multi-head grid decodes
+// when the batch is dealt by context length: ranked longest first (equal
+// lengths by index), then taken in runs of a.balance_run ranks whose
+// direction alternates.  With one round of workgroups, the items a compute
+// unit holds together are C / g sequence positions apart (C compute units, g
+// items per sequence, workgroups dealt round-robin); runs of that length give
+// every CU long and short contexts alike instead of leaving some CUs all
+// long ones.  `len` is sequence `lane`'s context length (lanes below
+// a.num_seqs <= 64).  A batch of equal lengths keeps the batch order.  Every
+// lane returns the same value.
+__device__ __forceinline__ int balanced_seq(const DecodeArgs& a, int pos, int len) {
+  const int lane = threadIdx.x & 63;
+  const int n = a.num_seqs;
+  const int cap = a.max_blocks * a.block_size;
+  len = lane < n ? min(max(len, 0), cap) : -1;
+  const int first = __builtin_amdgcn_readlane(len, 0);
+  if (__ballot(lane < n && len != first) == 0) return pos;
+  int rank = 0;
+  for (int j = 0; j < n; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += (lj > len || (lj == len && j < lane)) ? 1 : 0;
+  }
+  const int run = a.balance_run;
+  const int r0 = pos / run * run;
+  const int off = pos - r0;
+  const int target = ((pos / run) & 1) ? r0 + min(run, n - r0) - 1 - off : r0 + off;
+  const uint64_t hit = __ballot(lane < n && rank == target);
+  return hit ? static_cast<int>(__builtin_ctzll(hit)) : pos;
+}
 
 // The attended part of a sequence's context: its length clamped to the table,
 // the first attended token (the last `window` tokens when a sliding window is
@@ -452,13 +486,12 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   const int nsk = a.num_seqs * gps;
   const int part = item / nsk;
   const int sk = item - part * nsk;
-  const int seq = sk / gps;
-  const int kvh0 = (sk - seq * gps) * hpw;
+  const int pos = sk / gps;           // sequence position in the grid
+  const int kvh0 = (sk - pos * gps) * hpw;
   const int kvw = kvh0 + hsub * HR;   // the wave's first kv head
   const int lhead = sub / LPH;        // this lane's head within the load row
   const int kvh = kvw + lhead;        // this lane's kv head
 
-  const int32_t* trow = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks;
   // Issued together, before the context length is known, so that the
   // prologue waits for one memory round trip instead of three: this wave's
   // first table entries of the partition (as many as a full table holds;
@@ -466,22 +499,40 @@ __global__ void __launch_bounds__(NW * 64) paged_decode_kernel(DecodeArgs a) {
   // With a sliding window (or after a shared prefix) the partitions start at
   // a token that depends on the length, so the table is read after it.
   const bool early_table = a.window == 0 && !a.prefix_lens;
-  int tb_first = -1;
-  if (early_table) {
-    const int pb0e = part * part_blocks;
-    const int span_full = min(pb0e + part_blocks, a.max_blocks) - pb0e - wslot;
-    const int nk_full = span_full > 0 ? (span_full + wph - 1) / wph : 0;
-    if (lane < min(64, nk_full)) tb_first = trow[pb0e + wslot + wph * lane];
-  }
-
+  const int32_t* trow;
+  int tb_first;
   float qf[G][E];
+  Span sp;
+  auto prologue = [&](int s) {
+    trow = a.block_tables + static_cast<int64_t>(s) * a.max_blocks;
+    tb_first = -1;
+    if (early_table) {
+      const int pb0e = part * part_blocks;
+      const int span_full = min(pb0e + part_blocks, a.max_blocks) - pb0e - wslot;
+      const int nk_full = span_full > 0 ? (span_full + wph - 1) / wph : 0;
+      if (lane < min(64, nk_full)) tb_first = trow[pb0e + wslot + wph * lane];
+    }
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const int h = kvh * G + g;
-    load_q<QF, E>(a.q, (static_cast<int64_t>(seq) * a.num_heads + h) * D + (sub % LPH) * E, qf[g]);
+    for (int g = 0; g < G; ++g) {
+      const int h = kvh * G + g;
+      load_q<QF, E>(a.q, (static_cast<int64_t>(s) * a.num_heads + h) * D + (sub % LPH) * E, qf[g]);
+    }
+    sp = attended_span(a, s);
+  };
+  // With the length-balanced order every sequence's length is read in the
+  // same round trip as the prologue of the batch-order sequence `pos`, whose
+  // loads stand when the order keeps it (equal lengths).
+  int all_len = -1;
+  if (a.balance_run > 0 && lane < a.num_seqs) all_len = a.context_lens[lane];
+  int seq = pos;
+  prologue(seq);
+  if (a.balance_run > 0) {
+    const int s = balanced_seq(a, pos, all_len);
+    if (s != seq) {
+      seq = s;
+      prologue(seq);
+    }
   }
-
-  const Span sp = attended_span(a, seq);
   const int ctx = sp.ctx;
   if (part >= sp.nparts && part != 0) return;  // partition past the context
   const int pb0 = sp.origin / BS + part * part_blocks;

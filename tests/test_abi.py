@@ -300,7 +300,10 @@ def test_decode_plan_reports_the_launch():
     assert p["kv_heads_per_workgroup"] == 4 and p["workgroups"] == 32 * 16
     assert pkv.decode_plan(16, 64, 64, 128, 16, 4, pkv.I8)["kv_heads_per_workgroup"] == 2
     assert pkv.decode_plan(4, 64, 64, 128, 16, 4, pkv.I8)["kv_heads_per_workgroup"] == 1
-    assert pkv.decode_plan(32, 32, 32, 128, 16, 128, pkv.F16)["kv_heads_per_workgroup"] == 1
+    # 32 x 32 heads, fp16: one head per workgroup unless the device's CU count
+    # is known (then the length-balanced order and two heads; see
+    # test_gpu_balanced_order)
+    assert pkv.decode_plan(32, 32, 32, 128, 16, 128, pkv.F16)["kv_heads_per_workgroup"] in (1, 2)
     p = pkv.decode_plan(256, 32, 8, 128, 16, 256, pkv.I8)             # grouped-query, split
     assert p["kernel"] == "grouped_query" and p["kv_heads_per_workgroup"] == 1
     assert p["partition_tokens"] == pkv.decode_partition_size(256, 32, 8, 128, 16, 256) == 1024
