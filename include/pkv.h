@@ -181,10 +181,11 @@ int pkv_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
  *                so calls that share a workspace must be stream-ordered
  *
  * Scheduling (not part of the result): batches of 2..64 sequences decoded
- * by the multi-head kernel with whole contexts, whose grid fills the GPU's
- * compute units once to four times, are dealt to the workgroups by context
- * length (each workgroup reads all lengths), so that every compute unit gets
- * long and short contexts alike; equal lengths keep the batch order.
+ * by the multi-head kernel with whole contexts, tables of at least 1024
+ * tokens and a grid that fills the GPU's compute units once to four times,
+ * are dealt to the workgroups by context length (each workgroup reads all
+ * lengths), so that every compute unit gets long and short contexts alike;
+ * equal lengths keep the batch order.
  *
  * A block id outside [0, num_blocks) in a position that is read makes that
  * block's tokens count as masked (output unspecified but finite, no

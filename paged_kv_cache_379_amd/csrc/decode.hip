@@ -98,8 +98,8 @@ int device_cus() {
 // The multi-head kernel's plan: kv heads per workgroup and the run of the
 // length-balanced sequence order (balanced_seq; 0 keeps the batch order).
 // The order applies to batches of 2..64 sequences with whole contexts (one
-// partition) whose grid is one round of workgroups (at least one and at most
-// four per CU);
+// partition) of tables spanning at least kBalanceMinTokens tokens, whose grid
+// is one round of workgroups (at least one and at most four per CU);
 // its runs are the C / g sequence positions between the items one CU holds
 // (C compute units, g workgroups per sequence).  With the order in place two
 // heads per workgroup pay off down to one workgroup per CU.  Measured on
@@ -109,16 +109,22 @@ int device_cus() {
 // from the host; computed in the kernel it also reads every length before
 // the sequence's own loads); at uniform lengths two heads are faster as well
 // (1088 tokens: 93.4-94.5 against 95.9-97.0 us; 2048: 167.6-168.3 against
-// 173.5-174.4).
+// 173.5-174.4).  Short tables gain nothing: 32 x 32 heads of uniform 1..256 /
+// 1..512 / 1..1024 tokens took 20.2-20.3 / 30.3-31.0 / 51.2-52.1 us with the
+// order and two heads against 19.0-19.1 / 29.8-29.9 / 51.1-51.3 without.
+constexpr int64_t kBalanceMinTokens = 1024;
+
 struct MhaPlan {
   int hpi;
   int run;
 };
 
-MhaPlan mha_plan(int num_seqs, int num_heads, int num_kv_heads, int parts, int kv_dtype) {
+MhaPlan mha_plan(int num_seqs, int num_heads, int num_kv_heads, int parts, int kv_dtype,
+                 int64_t span) {
   MhaPlan p{mha_heads_per_item(num_seqs, num_heads, num_kv_heads, parts, kv_dtype), 0};
+  if (parts != 1 || num_seqs < 2 || num_seqs > 64 || span < kBalanceMinTokens) return p;
   const int cus = device_cus();
-  if (cus <= 0 || parts != 1 || num_seqs < 2 || num_seqs > 64) return p;
+  if (cus <= 0) return p;
   auto one_round = [&](int h) {
     const int64_t items = static_cast<int64_t>(num_seqs) * (num_kv_heads / h);
     return items >= cus && items <= 4 * static_cast<int64_t>(cus);
@@ -376,7 +382,7 @@ int pkv_decode_plan(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
   const int parts = static_cast<int>((span + pt - 1) / pt);
   const int group = num_heads / num_kv_heads;
   const bool vector = kv_dtype == PKV_F32 || group == 1;
-  const int hpi = vector ? mha_plan(num_seqs, num_heads, num_kv_heads, parts, kv_dtype).hpi : 1;
+  const int hpi = vector ? mha_plan(num_seqs, num_heads, num_kv_heads, parts, kv_dtype, span).hpi : 1;
   const int64_t items = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpi) * parts;
   if (items > INT32_MAX) return pkv::fail(PKV_ERR_INVALID_ARG, "grid too large");
   plan[0] = parts > 1 ? static_cast<int>(pt) : 0;
@@ -424,7 +430,7 @@ int pkv_paged_attention_decode(void* out, const void* q, const void* key_cache,
     return pkv::fail(PKV_ERR_WORKSPACE, "workspace needs %zu bytes (got %zu%s)", need,
                      workspace_bytes, workspace ? "" : ", NULL");
   const bool vector = kv_dtype == PKV_F32 || group == 1;
-  const MhaPlan mp = vector ? mha_plan(num_seqs, num_heads, num_kv_heads, parts, kv_dtype)
+  const MhaPlan mp = vector ? mha_plan(num_seqs, num_heads, num_kv_heads, parts, kv_dtype, span)
                             : MhaPlan{1, 0};
   const int hpi = mp.hpi;
   const int64_t items = static_cast<int64_t>(num_seqs) * (num_kv_heads / hpi) * parts;

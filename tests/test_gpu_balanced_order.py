@@ -1,5 +1,6 @@
-"""Multi-head decode of batches of at most 64 sequences with whole contexts
-that fill the GPU in one round of workgroups: the library deals the
+"""Multi-head decode of batches of at most 64 sequences with whole contexts,
+tables of at least 1024 tokens and a grid that fills the GPU in one round
+of workgroups: the library deals the
 sequences to the grid by context length (longest first, in runs whose
 direction alternates, so every CU gets long and short contexts) and, for
 16-bit caches, gives each workgroup two neighbouring kv heads.  Only which
@@ -19,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 def _workload(kv_fmt, q_fmt, lens, heads, head_dim, seed):
     lens = [int(x) for x in lens]
-    mb = (max(lens) + 15) // 16 + 1
+    mb = max((max(lens) + 15) // 16 + 1, 64)   # the order needs a table of >= 1024 tokens
     return W.make_workload(2, seed=seed, num_seqs=len(lens), num_heads=heads, num_kv_heads=heads,
                            head_dim=head_dim, kv_fmt=kv_fmt, q_fmt=q_fmt, ctx=("fixed", lens),
                            max_blocks=mb, poison_unused=True)
@@ -54,10 +55,12 @@ def test_balanced_order_parity(gpu_lib, kv_fmt, q_fmt, lens, heads, head_dim):
 def test_plan_uses_two_heads_with_the_order(gpu_lib):
     """On the GPU the 7B-like layer's shape (32 x 32 heads, fp16, whole
     contexts) runs two heads per workgroup, 512 workgroups; a batch whose
-    grid would not fill every CU once keeps one head."""
+    grid would not fill every CU once, or whose tables are shorter than 1024
+    tokens, keeps one head."""
     p = gpu_lib.decode_plan(32, 32, 32, 128, 16, 128, gpu_lib.F16)
     assert p["kv_heads_per_workgroup"] == 2 and p["workgroups"] == 512
-    assert gpu_lib.decode_plan(4, 32, 32, 128, 16, 20, gpu_lib.F16)["kv_heads_per_workgroup"] == 1
+    assert gpu_lib.decode_plan(4, 32, 32, 128, 16, 128, gpu_lib.F16)["kv_heads_per_workgroup"] == 1
+    assert gpu_lib.decode_plan(32, 32, 32, 128, 16, 32, gpu_lib.F16)["kv_heads_per_workgroup"] == 1
 
 
 def test_balanced_order_one_hot_bit_exact(gpu_lib):
@@ -70,8 +73,8 @@ def test_balanced_order_one_hot_bit_exact(gpu_lib):
     B, H, D, bs = 40, 32, 128, 16
     lens = rng.integers(1, 400, B)
     lens[:5] = 399                            # ties at the top of the order
-    mb = (int(lens.max()) + bs - 1) // bs
-    nb = B * mb + 3
+    mb = 64                                   # a 1024-token table (rows padded with -1)
+    nb = B * ((int(lens.max()) + bs - 1) // bs) + 3
     perm = rng.permutation(nb)
     tables = np.full((B, mb), -1, np.int32)
     pos = 0

@@ -1,7 +1,8 @@
 """Multi-head decode with several kv heads per workgroup: large enough
 batches make the library give each workgroup two neighbouring heads
 (16-bit caches, at least 1024 workgroups left, or at least one per CU for
-batches of at most 64 sequences dealt by length) or four (one-byte caches, at
+batches of at most 64 sequences with tables of 1024 tokens or more, dealt
+by length) or four (one-byte caches, at
 least 512 left), each head on its own waves.  Every output against the
 oracle, with ragged lengths, unread slots poisoned, partitions with the
 merge kernel, a sliding window, and head counts that two or four do not
