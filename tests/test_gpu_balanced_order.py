@@ -100,3 +100,26 @@ def test_balanced_order_one_hot_bit_exact(gpu_lib):
     want = np.stack([vc[tables[s, hot[s] // bs], hot[s] % bs] for s in range(B)])
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
     assert gpu_lib.decode_plan(B, H, H, D, bs, mb, gpu_lib.F16)["kv_heads_per_workgroup"] == 2
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_balanced_order_random_shapes(gpu_lib, case):
+    """Seeded random batches in the order's range (32..64 sequences, tables
+    of 1152 tokens, whole contexts): heads, head_dim, cache format and
+    lengths (an empty context included) drawn per case; every output against
+    the oracle.  Shapes whose grid is more than one round keep the batch
+    order, which the same comparison covers."""
+    rng = np.random.default_rng(1000 + case)
+    kv_fmt, q_fmt = [("f16", "f16"), ("bf16", "bf16"), ("fp8", "f16"), ("i8", "bf16"),
+                     ("f32", "f32")][case % 5]
+    B = int(rng.integers(32, 65))                    # with >= 16 heads: whole contexts
+    heads = int(rng.choice([16, 32, 64]))
+    head_dim = int(rng.choice([64, 128]))
+    lens = rng.integers(0, 1100, B)
+    lens[rng.integers(0, B)] = 0                     # an empty context
+    wl = W.make_workload(2, seed=2000 + case, num_seqs=B, num_heads=heads, num_kv_heads=heads,
+                         head_dim=head_dim, kv_fmt=kv_fmt, q_fmt=q_fmt,
+                         ctx=("fixed", [int(x) for x in lens]), max_blocks=72, poison_unused=True)
+    got = out_f64(gpu_decode(gpu_lib, wl))
+    assert_parity(got, oracle_decode(wl), kv_fmt, q_fmt, with_output_rounding=True,
+                  label=f"case {case}: {kv_fmt} B={B} H={heads} D={head_dim}")
