@@ -836,6 +836,8 @@ def main():
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for about {args.cpu_budget:.0f}s")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        # the GPU's rate over the oracle's, both in context tokens/s
+        result["cpu_baseline"]["gpu_speedup"] = result["value"] / result["cpu_baseline"]["value"]
     print(json.dumps(result), flush=True)
 
 
